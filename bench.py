@@ -1,0 +1,202 @@
+"""Throughput of the per-rank attention hot path on one MI355X.
+
+Headline: causal varlen attention forward on one rank's 8192-token packed slice (skewed length
+mix; GQA 32 query / 8 key-value heads; D = 128; bf16), as TFLOP/s of exact algorithmic FLOPs
+(hdp_seq_flops: 4*H*D per visible (query, key) pair) and as a fraction of the bf16 dense MFMA
+peak.  Method: W untimed warm-up steps, then K timed steps (defaults 20 and 200, the pages'
+own method: mean of 200 iterations after 20 warm-up), bracketed by device synchronisation.
+One step = one call of hdp_attn_varlen_fwd over the resident slice.
+
+Printed: one JSON line (rank 0).  `roofline.achieved` is the FLOPs of one launch divided by the
+kernel's mean duration from per-launch HIP events on the launch stream; `roofline.traffic` is
+the HBM byte count per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under
+profiles/ (null if absent or taken on a different kernel source).  `cpu_baseline` times the
+fp64 oracle on a bounded sample of the same slice on the host cores.  `detail` adds the other
+rows of the hot path (ring chunks + LSE merge, 32K micro-batches, backward) for context.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_packed_slice_8k.json")
+FWD_SRC = os.path.join(ROOT, "variable_length_attention_amd", "csrc", "fwd_bf16.hip")
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash(FWD_SRC):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def timed_launches(fn, steps: int, warmup: int, torch):
+    """Runs fn() warmup+steps times; returns (ms per step over the bracket, mean per-launch ms)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    outer0 = torch.cuda.Event(enable_timing=True)
+    outer1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    outer0.record()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    outer1.record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return outer0.elapsed_time(outer1) / steps, sum(per) / len(per)
+
+
+def cpu_baseline(w, q, k, v, cu):
+    """The fp64 oracle on every 2nd row of the slice (all heads), scaled to TFLOP/s."""
+    import numpy as np
+
+    import oracle
+
+    rows = np.arange(0, int(cu[-1]), 2, dtype=np.int64)
+    seq = np.searchsorted(cu, rows, side="right") - 1
+    pairs = int(np.sum(rows - cu[seq] + 1))
+    flops = pairs * w.H * 4 * w.D
+    t0 = time.perf_counter()
+    oracle.varlen_fwd(q, k, v, cu, w.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "every 2nd query row of the same 8192-token slice, all 32 heads "
+                      "(%d rows, %.3g FLOP, %.1f s)" % (len(rows), flops, dt)}
+
+
+def detail_rows(torch, ops, synth, steps: int, warmup: int):
+    """Other rows of the hot path, timed the same way (context, not the headline)."""
+    out = {}
+    # ring-chunk share: 16 chunk partials + 15 LSE merges
+    w = synth.ring_chunks_128k()
+    q, k, v = (t.cuda() for t in synth.ring_tensors(w))
+    L = w.chunk_len
+    acc_o = torch.empty((w.q_len, w.H, w.D), dtype=torch.float32, device="cuda")
+    acc_l = torch.empty((w.q_len, w.H), dtype=torch.float32, device="cuda")
+    po, pl = torch.empty_like(acc_o), torch.empty_like(acc_l)
+    chunks = [(k[c * L:(c + 1) * L], v[c * L:(c + 1) * L]) for c in range(w.n_chunks)]
+
+    def ring_step():
+        ops.hdp_attn_chunk_partial(q, chunks[0][0], chunks[0][1], w.q_offset, 0, True, w.scale,
+                                   o_partial=acc_o, lse=acc_l)
+        for c in range(1, w.n_chunks):
+            ops.hdp_attn_chunk_partial(q, chunks[c][0], chunks[c][1], w.q_offset, c * L, True,
+                                       w.scale, o_partial=po, lse=pl)
+            ops.hdp_lse_merge(acc_o, acc_l, po, pl)
+
+    rs = max(5, steps // 20)
+    ms, _ = timed_launches(ring_step, rs, max(2, warmup // 10), torch)
+    fl = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D) for c in range(w.n_chunks))
+    _, merge_ms = timed_launches(lambda: ops.hdp_lse_merge(acc_o, acc_l, po, pl), steps, warmup, torch)
+    merge_bytes = w.q_len * w.H * (12 * w.D + 12)
+    out["ring_chunks_128k"] = {"ms_per_step": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                               "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                               "merge_us": merge_ms * 1e3,
+                               "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9}
+    del q, k, v, chunks, acc_o, acc_l, po, pl
+    for make in (synth.microbatch_32k_long, synth.microbatch_32k_short):
+        w = make()
+        qq, kk, vv = (t.cuda() for t in synth.varlen_tensors(w))
+        cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
+        o = torch.empty_like(qq)
+        lse = torch.empty((qq.shape[0], w.H), dtype=torch.float32, device="cuda")
+        _, ms = timed_launches(lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse),
+                               steps // 4, warmup, torch)
+        fl = sum(ops.hdp_seq_flops(s, w.H, w.D) for s in w.lengths)
+        out[w.name] = {"n_seq": len(w.lengths), "GFLOP": fl / 1e9, "kernel_us": ms * 1e3,
+                       "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the per-rank kernel "
+              "is the unit; a ring would move K/V between GPUs over RCCL). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from variable_length_attention_amd import ops, synth
+
+    torch.cuda.set_device(0)
+    w = synth.packed_slice_8k()
+    q, k, v = synth.varlen_tensors(w)
+    cu = synth.cu_seqlens(w.lengths)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    cug = torch.from_numpy(cu).cuda()
+    out = torch.empty_like(qg)
+    lse = torch.empty((qg.shape[0], w.H), dtype=torch.float32, device="cuda")
+    flops = sum(ops.hdp_seq_flops(s, w.H, w.D) for s in w.lengths)
+
+    def step():
+        ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale, out=out, lse=lse)
+
+    ms_step, ms_kernel = timed_launches(step, args.steps, args.warmup, torch)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    result = {
+        "metric": "varlen attn TFLOP/s on 8K-token packed slice; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "packed_slice_8k: one rank's 8192-token slice, %d causal sequences "
+                               "%s, H=32 Hkv=8 D=128 bf16, forward" % (len(w.lengths), w.lengths),
+                   "tokens": int(cu[-1]), "n_seq": len(w.lengths), "gflop": round(flops / 1e9, 3),
+                   "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": load_traffic(), "kernel_us": round(ms_kernel * 1e3, 2)},
+    }
+    if not args.no_detail:
+        result["detail"] = detail_rows(torch, ops, synth, args.steps, args.warmup)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,144 @@
+/*
+ * hdp_attn.h -- C ABI of the per-rank attention library for Hybrid Data Parallelism on
+ * MI355X (gfx950).  Library: variable_length_attention_amd/libhdpattn.so.
+ *
+ * What is computed.  Under Hybrid Data Parallelism every rank holds a slice of at most C
+ * tokens.  Sequences no longer than C sit whole on one rank, packed back to back, and send
+ * nothing; a longer sequence spans ceil(s/C) ranks that pass key/value slices around their own
+ * ring (research digest "ByteScale: Communication-Efficient Scaling of LLM Training with a
+ * 2048K Context Length on 16384 GPUs", §3.1 and Figure 2).  A query attends only to its own
+ * sequence, and a ring step computes on the K/V slice in hand while the next one arrives
+ * (same digest, §3.2).  The mask is causal (same digest, §4).  Attention work grows with the
+ * square of each sequence's length (same digest, §2), which is what hdp_seq_flops counts.
+ *
+ * The pages print no formula; the library computes textbook scaled-dot-product attention:
+ * for query row r and the keys j it may see,
+ *     out_r = sum_j softmax_j(scale * <q_r, k_j>) v_j,   lse_r = ln sum_j exp(scale * <q_r, k_j>).
+ * Query head h reads key/value head h / (H / Hkv) (contiguous groups).
+ *
+ * Conventions for every call.
+ *   - Tensor pointers are DEVICE memory owned by the caller; the library keeps no reference
+ *     after the call returns and frees nothing it did not allocate.
+ *   - bf16 tensors are stored as uint16_t bit patterns; outputs are rounded to nearest even.
+ *   - Layouts are token-major and dense: q/out/dq [T][H][D], k/v/dk/dv [T][Hkv][D],
+ *     lse [T][H] fp32.  Within one token all heads are contiguous.
+ *   - Every call is asynchronous on `stream` (0 = the null stream) and never synchronises the
+ *     host.  Device faults surface at the caller's next synchronisation.
+ *   - Arguments are checked on the host before any HIP call.  Errors return a status and
+ *     launch nothing.  n_seq == 0 or Lq == 0 is a no-op returning HDP_OK.
+ *   - cu_seqlens is device memory (int32, n_seq + 1 entries, cu[0] = 0, non-decreasing,
+ *     T = cu[n_seq]).  Its contents are not checked on the host; the kernels clamp every
+ *     sequence to [0, cu[n_seq]], so malformed entries give empty sequences, never an access
+ *     outside rows 0 .. cu[n_seq]-1.  Rows outside [cu[0], cu[n_seq]) are left untouched.
+ *   - Supported head dims: D = 64 and D = 128 (else HDP_ERR_UNSUPPORTED).
+ *   - The library owns one small workspace per device (work-queue counters and, for the
+ *     backward, an fp32 dQ accumulator), grown on demand.  Calls that overlap in time on one
+ *     device (different streams or host threads) share it and must not run concurrently.
+ *     hdp_release_workspace() frees it.
+ */
+#ifndef HDP_ATTN_H
+#define HDP_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HDP_OK = 0,
+    HDP_ERR_INVALID_ARG = 1, /* null pointer with work to do, bad sizes, H % Hkv != 0, ... */
+    HDP_ERR_UNSUPPORTED = 2, /* head dim other than 64 / 128 */
+    HDP_ERR_HIP = 3,         /* a HIP launch or allocation failed */
+    HDP_ERR_OVERFLOW = 4     /* a size product does not fit the index types */
+} hdp_status_t;
+
+enum { HDP_PASS_FWD = 0, HDP_PASS_BWD = 1, HDP_PASS_FWD_BWD = 2 };
+
+/*
+ * Packed variable-length causal attention, forward, bf16 in / bf16 out, fp32 accumulation.
+ * Sequence i owns packed rows cu[i] .. cu[i+1]-1; row r of it sees rows cu[i] .. cu[i]+r of
+ * the same sequence and nothing else (digest §3.1-§3.2: a query attends only to its own
+ * sequence; packed short sequences need no partner).
+ *   q [T][H][D], k, v [T][Hkv][D] bf16; out [T][H][D] bf16 (written); lse [T][H] fp32, natural
+ *   log of the row's sum of exp(scale * score) (written).  scale must be finite.
+ * Work is split into (sequence, head group, query tile) items whose cost is the number of key
+ * tiles they visit (the tile form of hdp_seq_flops); the kernel pops them longest first.
+ */
+int hdp_attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                        int32_t n_seq, int32_t H, int32_t Hkv, int32_t D, float scale,
+                        void* out, float* lse, hipStream_t stream);
+
+/* Same as hdp_attn_varlen_fwd with fp32 q, k, v and fp32 out (fp32 arithmetic throughout). */
+int hdp_attn_varlen_fwd_f32(const float* q, const float* k, const float* v,
+                            const int32_t* cu_seqlens, int32_t n_seq, int32_t H, int32_t Hkv,
+                            int32_t D, float scale, float* out, float* lse, hipStream_t stream);
+
+/*
+ * One ring step (digest §3.2): a slice of Lq query tokens of one long sequence, at global
+ * positions q_offset + r, against one key/value chunk of Lk tokens at global positions
+ * kv_offset + j.  With causal != 0, key j is visible to row r iff kv_offset + j <= q_offset + r;
+ * with causal == 0 every key is visible.
+ *   q_slice [Lq][H][D], k_chunk, v_chunk [Lk][Hkv][D] bf16.
+ *   o_partial [Lq][H][D] fp32 (written): the softmax average over this chunk's visible keys.
+ *   lse [Lq][H] fp32 (written).  A row with no visible key gets o = 0 and lse = -inf.
+ * Combine the steps with hdp_lse_merge.  Offsets must be >= 0.
+ */
+int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
+                           const void* v_chunk, int32_t Lk, int64_t q_offset, int64_t kv_offset,
+                           int32_t causal, int32_t H, int32_t Hkv, int32_t D, float scale,
+                           float* o_partial, float* lse, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of two partials over disjoint key sets, in place (the ring's per-step
+ * combination, digest §3.2).  For each of the L*H (token, head) rows:
+ *     m = max(l_acc, l_part); w = exp(l - m); o_acc = (w_acc o_acc + w_part o_part)/(w_acc + w_part);
+ *     l_acc = m + ln(w_acc + w_part).
+ * A partial with lse = -inf is the identity (two empty partials stay 0 / -inf, never NaN).
+ *   o_acc [L][H][D], lse_acc [L][H] fp32: read and overwritten.
+ *   o_part [L][H][D], lse_part [L][H] fp32: read only.
+ *   out_bf16: NULL, or [L][H][D] bf16 that receives the merged o_acc rounded to bf16.
+ */
+int hdp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                  int32_t L, int32_t H, int32_t D, void* out_bf16, hipStream_t stream);
+
+/*
+ * Backward of hdp_attn_varlen_fwd (the pages show forward and backward time per step but give
+ * no formulas; this is the chain rule of the forward above).  With P = exp(scale*S - lse):
+ *     dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * out)),  dQ = scale dS K,  dK = scale dS^T Q,
+ * dK and dV summed over the H/Hkv query heads of each key/value head.
+ *   q, k, v, out, dout bf16 as in the forward; lse fp32 [T][H] from the forward.
+ *   T: total packed tokens (the caller's row count, = cu[n_seq]); sizes the fp32 workspace and
+ *   bounds every access (sequences are clamped to rows 0 .. T-1).
+ *   dq [T][H][D], dk, dv [T][Hkv][D] bf16 (written).
+ */
+int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, const void* dout, const int32_t* cu_seqlens,
+                        int32_t n_seq, int32_t T, int32_t H, int32_t Hkv, int32_t D,
+                        float scale, void* dq, void* dk, void* dv, hipStream_t stream);
+
+/*
+ * Exact attention FLOPs of one sequence of s tokens attending to itself: visible pairs
+ * P = s(s+1)/2 (causal) or s^2, times H, times 4D (forward: score and value contractions),
+ * 10D (backward: five contractions) or 14D (both).  The O(s^2) cost that drives data-aware
+ * sharding and the balance scheduler (digest §2, §3.4).  Returns 0 for s <= 0, H <= 0 or
+ * D <= 0, and UINT64_MAX on overflow or an unknown pass.
+ */
+uint64_t hdp_seq_flops(int64_t s, int32_t H, int32_t D, int32_t causal, int32_t pass);
+
+/* FLOPs of one ring step (as hdp_attn_chunk_partial counts visible pairs), same units. */
+uint64_t hdp_chunk_flops(int32_t Lq, int32_t Lk, int64_t q_offset, int64_t kv_offset,
+                         int32_t causal, int32_t H, int32_t D, int32_t pass);
+
+/* Static text for a status code. */
+const char* hdp_status_string(int status);
+
+/* Frees the calling thread's current device's workspace (synchronises that device). */
+int hdp_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HDP_ATTN_H */

@@ -1,0 +1,42 @@
+"""Helpers shared by the GPU parity tests (no attention arithmetic here)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# Tolerances (max-abs): bf16 inputs with fp32 accumulation; fp32 end to end.
+TOL_BF16_OUT = 2e-2
+TOL_BF16_LSE = 1e-3
+TOL_F32 = 1e-5
+
+
+def to_gpu(*ts):
+    return [t.to("cuda") for t in ts]
+
+
+def max_abs(gpu_t, ref: np.ndarray) -> float:
+    g = gpu_t.detach().float().cpu().double().numpy()
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def sample_rows(cu, stride: int = 8):
+    """Every stride-th packed row plus the first and last row of every sequence (sorted)."""
+    cu = [int(x) for x in cu]
+    T = cu[-1]
+    rows = set(range(0, T, stride))
+    for i in range(len(cu) - 1):
+        if cu[i + 1] > cu[i]:
+            rows.add(cu[i])
+            rows.add(cu[i + 1] - 1)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def lse_close(gpu_lse, ref: np.ndarray, tol: float) -> float:
+    """Max-abs error of an lse tensor, treating matching -inf entries as exact."""
+    g = gpu_lse.detach().float().cpu().double().numpy()
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref)), "-inf pattern differs"
+    d = np.where(both_inf, 0.0, np.abs(g - np.where(both_inf, 0.0, ref)))
+    err = float(np.max(d)) if d.size else 0.0
+    assert err <= tol, err
+    return err

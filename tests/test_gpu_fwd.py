@@ -1,0 +1,225 @@
+"""GPU parity of the forward paths against the fp64 oracle, through the C ABI.
+
+Small cases compare every element; the full-size workloads compare a deterministic row sample
+(every 8th/16th/64th packed row plus the first and last row of every sequence, all heads) that
+the oracle evaluates row by row.  Exactness properties of the packing (a query attends only to
+its own sequence) are checked bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, TOL_F32, lse_close, max_abs, sample_rows, to_gpu
+from variable_length_attention_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def varlen_case(lengths, H, Hkv, D, seed, dtype="bf16"):
+    w = synth.Workload("case", "varlen", H, Hkv, D, dtype, list(lengths), seed)
+    q, k, v = synth.varlen_tensors(w)
+    cu = synth.cu_seqlens(w.lengths)
+    return w, q, k, v, cu
+
+
+def run_fwd(q, k, v, cu, scale):
+    qg, kg, vg = to_gpu(q, k, v)
+    cug = torch.from_numpy(cu).to("cuda")
+    out, lse = ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_tiny_fp32_pack_full():
+    w = synth.tiny_fp32_pack()
+    q, k, v = synth.varlen_tensors(w)
+    cu = synth.cu_seqlens(w.lengths)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    qg, kg, vg = to_gpu(q, k, v)
+    out, lse = ops.hdp_attn_varlen_fwd_f32(qg, kg, vg, torch.from_numpy(cu).cuda(), w.scale)
+    torch.cuda.synchronize()
+    assert max_abs(out, ro) <= TOL_F32
+    assert max_abs(lse, rl) <= TOL_F32
+
+
+RAGGED = [1, 17, 64, 65, 127, 128, 129, 300, 0, 513, 31]
+
+
+@pytest.mark.parametrize("H,Hkv,D", [(32, 8, 128), (8, 8, 64), (4, 2, 128), (16, 2, 64),
+                                     (6, 2, 64), (32, 8, 64)])
+def test_bf16_ragged_pack_full(H, Hkv, D):
+    w, q, k, v, cu = varlen_case(RAGGED, H, Hkv, D, seed=11)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    e_out = max_abs(out, ro)
+    e_lse = max_abs(lse, rl)
+    print("H=%d Hkv=%d D=%d max|dout|=%.3g max|dlse|=%.3g" % (H, Hkv, D, e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+
+
+@pytest.mark.parametrize("make,stride", [(synth.packed_slice_8k, 8),
+                                         (synth.microbatch_32k_short, 16),
+                                         (synth.microbatch_32k_long, 64)])
+def test_full_size_workloads_sampled(make, stride):
+    w = make()
+    q, k, v = synth.varlen_tensors(w)
+    cu = synth.cu_seqlens(w.lengths)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    rows = sample_rows(cu, stride)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    e_out = max_abs(out[idx], ro)
+    e_lse = max_abs(lse[idx], rl)
+    print("%s: %d sampled rows, max|dout|=%.3g max|dlse|=%.3g" % (w.name, len(rows), e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_rows_depend_only_on_their_own_sequence_bitwise():
+    # Perturb one sequence (including NaN) and check every other row is bit-identical.
+    lengths = [100, 257, 64, 3, 190]
+    w, q, k, v, cu = varlen_case(lengths, 32, 8, 128, seed=12)
+    out0, lse0 = run_fwd(q, k, v, cu, w.scale)
+    a, b = int(cu[1]), int(cu[2])
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[a:b] = float("nan")
+    k2[a:b] = 3.0
+    v2[a:b] = float("nan")
+    out1, lse1 = run_fwd(q2, k2, v2, cu, w.scale)
+    keep = torch.ones(int(cu[-1]), dtype=torch.bool)
+    keep[a:b] = False
+    keep = keep.cuda()
+    assert torch.equal(out0[keep].view(torch.int16), out1[keep].view(torch.int16))
+    assert torch.equal(lse0[keep].view(torch.int32), lse1[keep].view(torch.int32))
+
+
+def test_sequence_permutation_permutes_rows_bitwise():
+    lengths = [100, 257, 64, 3, 190, 1]
+    w, q, k, v, cu = varlen_case(lengths, 32, 8, 128, seed=13)
+    out0, lse0 = run_fwd(q, k, v, cu, w.scale)
+    perm = [4, 2, 0, 5, 1, 3]
+    spans = [(int(cu[i]), int(cu[i + 1])) for i in range(len(lengths))]
+    idx = np.concatenate([np.arange(*spans[p]) for p in perm])
+    cu2 = synth.cu_seqlens([lengths[p] for p in perm])
+    out1, lse1 = run_fwd(q[idx], k[idx], v[idx], cu2, w.scale)
+    ig = torch.from_numpy(idx).cuda()
+    assert torch.equal(out0[ig].view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0[ig].view(torch.int32), lse1.view(torch.int32))
+
+
+def test_every_row_is_written_and_runs_are_deterministic():
+    w, q, k, v, cu = varlen_case([5, 700, 64, 0, 129], 32, 8, 128, seed=14)
+    qg, kg, vg = to_gpu(q, k, v)
+    cug = torch.from_numpy(cu).cuda()
+    out = torch.full_like(qg, float("nan"))
+    lse = torch.full((qg.shape[0], 32), float("nan"), device="cuda")
+    ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale, out=out, lse=lse)
+    out2, lse2 = ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
+def test_empty_and_single_token_sequences():
+    w, q, k, v, cu = varlen_case([0, 1, 0, 0, 1, 2, 0], 32, 8, 128, seed=15)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    assert max_abs(out, ro) <= TOL_BF16_OUT and max_abs(lse, rl) <= TOL_BF16_LSE
+
+
+# ------------------------------------------------------------------ ring chunks
+
+
+CHUNK_CASES = [
+    # (Lq, Lk, q_offset, kv_offset, causal)
+    (200, 192, 0, 0, True),        # diagonal chunk
+    (200, 192, 1000, 0, True),     # fully visible chunk
+    (200, 192, 0, 500, True),      # chunk in the future: nothing visible
+    (200, 192, 100, 150, True),    # partly visible, some rows empty
+    (130, 70, 0, 1000, False),     # no mask
+    (33, 65, 7, 3, True),          # ragged sizes
+    (64, 0, 0, 0, True),           # empty chunk
+]
+
+
+@pytest.mark.parametrize("Lq,Lk,q_off,kv_off,causal", CHUNK_CASES)
+@pytest.mark.parametrize("D", [128, 64])
+def test_chunk_partial_full(Lq, Lk, q_off, kv_off, causal, D):
+    H, Hkv = 32, 8
+    rng = np.random.default_rng(21)
+    q = synth.normal(rng, (Lq, H, D), "bf16")
+    k = synth.normal(rng, (Lk, Hkv, D), "bf16")
+    v = synth.normal(rng, (Lk, Hkv, D), "bf16")
+    scale = 1 / math.sqrt(D)
+    ro, rl = oracle.chunk_partial(q, k, v, q_off, kv_off, causal, scale)
+    qg, kg, vg = to_gpu(q, k, v)
+    o, lse = ops.hdp_attn_chunk_partial(qg, kg, vg, q_off, kv_off, causal, scale)
+    torch.cuda.synchronize()
+    assert max_abs(o, ro) <= TOL_BF16_OUT
+    lse_close(lse, rl, TOL_BF16_LSE)
+
+
+def test_ring_128k_share_merged_equals_full_causal_attention_sampled():
+    # One rank's share of a 16-rank ring over a 131072-token sequence: its 8192 queries at
+    # offset 122880 attend to 16 chunks of 8192 keys; merged partials = full causal attention.
+    w = synth.ring_chunks_128k()
+    q, k, v = synth.ring_tensors(w)
+    qg, kg, vg = to_gpu(q, k, v)
+    L = w.chunk_len
+    acc_o, acc_l = ops.hdp_attn_chunk_partial(qg, kg[:L], vg[:L], w.q_offset, 0, True, w.scale)
+    part_o = torch.empty_like(acc_o)
+    part_l = torch.empty_like(acc_l)
+    out_bf16 = torch.empty(acc_o.shape, dtype=torch.bfloat16, device="cuda")
+    keep = {}
+    for c in range(1, w.n_chunks):
+        ops.hdp_attn_chunk_partial(qg, kg[c * L:(c + 1) * L], vg[c * L:(c + 1) * L], w.q_offset,
+                                   c * L, True, w.scale, o_partial=part_o, lse=part_l)
+        if c in (3, 15):
+            keep[c] = (part_o.clone(), part_l.clone())
+        ops.hdp_lse_merge(acc_o, acc_l, part_o, part_l,
+                          out_bf16=out_bf16 if c == w.n_chunks - 1 else None)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, w.q_len, 512), [1, 2, 4095, 4096, w.q_len - 1]]))
+    idx = torch.from_numpy(rows).cuda()
+    ro, rl = oracle.chunk_partial(q, k, v, w.q_offset, 0, True, w.scale, rows=rows)
+    e_o = max_abs(acc_o[idx], ro)
+    e_b = max_abs(out_bf16[idx], ro)
+    e_l = max_abs(acc_l[idx], rl)
+    print("ring merged: rows=%d max|do|=%.3g max|dbf16|=%.3g max|dlse|=%.3g" % (len(rows), e_o, e_b, e_l))
+    assert e_o <= TOL_BF16_OUT and e_b <= TOL_BF16_OUT and e_l <= TOL_BF16_LSE
+    for c, (po, pl) in keep.items():
+        co, cl = oracle.chunk_partial(q, k[c * L:(c + 1) * L], v[c * L:(c + 1) * L], w.q_offset,
+                                      c * L, True, w.scale, rows=rows)
+        assert max_abs(po[idx], co) <= TOL_BF16_OUT
+        lse_close(pl[idx], cl, TOL_BF16_LSE)
+
+
+# ------------------------------------------------------------------------ merge
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_lse_merge_matches_oracle_including_empty_partials(D):
+    L, H = 300, 4
+    rng = np.random.default_rng(31)
+    o1 = rng.standard_normal((L, H, D)).astype(np.float32)
+    o2 = rng.standard_normal((L, H, D)).astype(np.float32)
+    l1 = (rng.standard_normal((L, H)) * 5).astype(np.float32)
+    l2 = (rng.standard_normal((L, H)) * 5).astype(np.float32)
+    l1[:20] = -np.inf
+    o1[:20] = 0
+    l2[10:30] = -np.inf
+    o2[10:30] = 0
+    ro, rl = oracle.lse_merge(o1, l1, o2, l2)
+    go, gl, po, pl = (torch.from_numpy(x).cuda() for x in (o1, l1, o2, l2))
+    bf = torch.empty(go.shape, dtype=torch.bfloat16, device="cuda")
+    ops.hdp_lse_merge(go, gl, po, pl, out_bf16=bf)
+    torch.cuda.synchronize()
+    assert max_abs(go, ro) <= 1e-5
+    lse_close(gl, rl, 1e-5)
+    ref_bf = torch.from_numpy(ro).float().to(torch.bfloat16).double().numpy()
+    assert max_abs(bf, ref_bf) <= TOL_BF16_OUT
+    assert not torch.isnan(go).any()

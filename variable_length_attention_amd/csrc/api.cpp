@@ -1,0 +1,286 @@
+// C ABI of the per-rank attention library: argument checks, per-device workspace, FLOP cost
+// model and kernel launches.  Every check happens on the host before any HIP call.
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "hdp_attn.h"
+#include "hdp_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DeviceState {
+    int cus = 0;
+    int* counters = nullptr;   // hdp::kCounterInts ints, zero between launches
+    void* ws = nullptr;        // backward workspace
+    size_t ws_bytes = 0;
+};
+
+std::mutex g_mu;
+std::unordered_map<int, DeviceState> g_dev;
+
+// Returns the calling thread's current device state, creating the counters on first use.
+int device_state(DeviceState** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return HDP_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DeviceState& st = g_dev[dev];
+    if (st.counters == nullptr) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return HDP_ERR_HIP;
+        int* c = nullptr;
+        if (hipMalloc(&c, sizeof(int) * hdp::kCounterInts) != hipSuccess) return HDP_ERR_HIP;
+        if (hipMemset(c, 0, sizeof(int) * hdp::kCounterInts) != hipSuccess ||
+            hipDeviceSynchronize() != hipSuccess) {
+            (void)hipFree(c);
+            return HDP_ERR_HIP;
+        }
+        st.cus = cus;
+        st.counters = c;
+    }
+    *out = &st;
+    return HDP_OK;
+}
+
+// Grows the backward workspace to at least `bytes` (synchronises the device when it grows).
+int ensure_workspace(DeviceState* st, size_t bytes) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (st->ws_bytes >= bytes) return HDP_OK;
+    if (std::getenv("HDP_TEST_FAIL_ALLOC") != nullptr) return HDP_ERR_HIP;
+    if (st->ws != nullptr) {
+        if (hipDeviceSynchronize() != hipSuccess) return HDP_ERR_HIP;
+        (void)hipFree(st->ws);
+        st->ws = nullptr;
+        st->ws_bytes = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return HDP_ERR_HIP;
+    st->ws = p;
+    st->ws_bytes = bytes;
+    return HDP_OK;
+}
+
+bool head_dim_ok(int D) { return D == 64 || D == 128; }
+
+int check_heads(int32_t H, int32_t Hkv, int32_t D) {
+    if (H <= 0 || Hkv <= 0 || D <= 0 || H % Hkv != 0) return HDP_ERR_INVALID_ARG;
+    if (!head_dim_ok(D)) return HDP_ERR_UNSUPPORTED;
+    return HDP_OK;
+}
+
+// Query heads per workgroup item: 4 when a key/value head serves a multiple of 4 query heads.
+int heads_per_item(int32_t H, int32_t Hkv) {
+    const int G = H / Hkv;
+    return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+}
+
+void schedule(const DeviceState* st, int32_t H, int32_t Hkv, hdp::FwdArgs& a, int& grid) {
+    a.hpw = heads_per_item(H, Hkv);
+    grid = st->cus;
+    const int nhb = H / a.hpw;
+    a.nqueues = (nhb % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0) ? hdp::kMaxQueues : 1;
+    a.counters = st->counters;
+}
+
+// sum_{r=0}^{n-1} clamp(a + r, 0, cap), exactly.
+unsigned __int128 sum_clamped(int64_t a, int64_t n, int64_t cap) {
+    if (n <= 0 || cap <= 0) return 0;
+    // r in [r1, r2): 0 < a + r < cap contributes a + r; r in [r2, n): contributes cap.
+    int64_t r1 = std::max<int64_t>(0, 1 - a);
+    int64_t r2 = std::max<int64_t>(0, cap - a);
+    r1 = std::min(r1, n);
+    r2 = std::min(std::max(r2, r1), n);
+    const __int128 cnt = (__int128)(r2 - r1);
+    const __int128 first = (__int128)a + r1;
+    const __int128 last = (__int128)a + r2 - 1;
+    __int128 s = cnt > 0 ? (first + last) * cnt / 2 : 0;
+    s += (__int128)(n - r2) * cap;
+    return (unsigned __int128)s;
+}
+
+uint64_t flops_from_pairs(unsigned __int128 pairs, int32_t H, int32_t D, int32_t pass) {
+    uint64_t per;
+    if (pass == HDP_PASS_FWD) per = 4ull * (uint64_t)D;
+    else if (pass == HDP_PASS_BWD) per = 10ull * (uint64_t)D;
+    else if (pass == HDP_PASS_FWD_BWD) per = 14ull * (uint64_t)D;
+    else return UINT64_MAX;
+    const unsigned __int128 f = pairs * (unsigned __int128)(uint64_t)H * per;
+    if (f > (unsigned __int128)UINT64_MAX) return UINT64_MAX;
+    return (uint64_t)f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hdp_status_string(int status) {
+    switch (status) {
+        case HDP_OK: return "HDP_OK";
+        case HDP_ERR_INVALID_ARG: return "HDP_ERR_INVALID_ARG: invalid argument";
+        case HDP_ERR_UNSUPPORTED: return "HDP_ERR_UNSUPPORTED: unsupported head dim (64 or 128)";
+        case HDP_ERR_HIP: return "HDP_ERR_HIP: HIP launch or allocation failed";
+        case HDP_ERR_OVERFLOW: return "HDP_ERR_OVERFLOW: size does not fit the index types";
+        default: return "unknown hdp status";
+    }
+}
+
+uint64_t hdp_seq_flops(int64_t s, int32_t H, int32_t D, int32_t causal, int32_t pass) {
+    if (pass != HDP_PASS_FWD && pass != HDP_PASS_BWD && pass != HDP_PASS_FWD_BWD) return UINT64_MAX;
+    if (s <= 0 || H <= 0 || D <= 0) return 0;
+    const unsigned __int128 us = (unsigned __int128)s;
+    const unsigned __int128 pairs = causal ? us * (us + 1) / 2 : us * us;
+    return flops_from_pairs(pairs, H, D, pass);
+}
+
+uint64_t hdp_chunk_flops(int32_t Lq, int32_t Lk, int64_t q_offset, int64_t kv_offset,
+                         int32_t causal, int32_t H, int32_t D, int32_t pass) {
+    if (pass != HDP_PASS_FWD && pass != HDP_PASS_BWD && pass != HDP_PASS_FWD_BWD) return UINT64_MAX;
+    if (Lq <= 0 || Lk <= 0 || H <= 0 || D <= 0) return 0;
+    unsigned __int128 pairs;
+    if (causal) {
+        // row r sees keys j with kv_offset + j <= q_offset + r: clamp(q_offset - kv_offset + 1 + r, 0, Lk)
+        const __int128 a = (__int128)q_offset - kv_offset + 1;
+        if (a > (__int128)INT64_MAX / 2 || a < (__int128)INT64_MIN / 2) return UINT64_MAX;
+        pairs = sum_clamped((int64_t)a, Lq, Lk);
+    } else {
+        pairs = (unsigned __int128)Lq * (unsigned __int128)Lk;
+    }
+    return flops_from_pairs(pairs, H, D, pass);
+}
+
+int hdp_attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                        int32_t n_seq, int32_t H, int32_t Hkv, int32_t D, float scale,
+                        void* out, float* lse, hipStream_t stream) {
+    if (n_seq < 0) return HDP_ERR_INVALID_ARG;
+    if (int st = check_heads(H, Hkv, D)) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (n_seq == 0) return HDP_OK;
+    if (!q || !k || !v || !cu_seqlens || !out || !lse) return HDP_ERR_INVALID_ARG;
+    DeviceState* st = nullptr;
+    if (int rc = device_state(&st)) return rc;
+    hdp::FwdArgs a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.cu = cu_seqlens;
+    a.n_seq = n_seq;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.scale_log2 = scale * kLog2e;
+    a.out = out;
+    a.lse = lse;
+    a.causal = 1;
+    int grid = 0;
+    schedule(st, H, Hkv, a, grid);
+    return hdp::launch_fwd_varlen(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+int hdp_attn_varlen_fwd_f32(const float* q, const float* k, const float* v,
+                            const int32_t* cu_seqlens, int32_t n_seq, int32_t H, int32_t Hkv,
+                            int32_t D, float scale, float* out, float* lse, hipStream_t stream) {
+    if (n_seq < 0) return HDP_ERR_INVALID_ARG;
+    if (int st = check_heads(H, Hkv, D)) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (n_seq == 0) return HDP_OK;
+    if (!q || !k || !v || !cu_seqlens || !out || !lse) return HDP_ERR_INVALID_ARG;
+    if (H > 65535) return HDP_ERR_OVERFLOW;
+    hdp::F32Args a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu = cu_seqlens;
+    a.n_seq = n_seq;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.scale_log2 = scale * kLog2e;
+    a.out = out;
+    a.lse = lse;
+    return hdp::launch_fwd_f32(a, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
+                           const void* v_chunk, int32_t Lk, int64_t q_offset, int64_t kv_offset,
+                           int32_t causal, int32_t H, int32_t Hkv, int32_t D, float scale,
+                           float* o_partial, float* lse, hipStream_t stream) {
+    if (Lq < 0 || Lk < 0 || q_offset < 0 || kv_offset < 0) return HDP_ERR_INVALID_ARG;
+    if (int st = check_heads(H, Hkv, D)) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (q_offset > INT64_MAX / 4 || kv_offset > INT64_MAX / 4) return HDP_ERR_OVERFLOW;
+    if (Lq == 0) return HDP_OK;
+    if (!q_slice || !o_partial || !lse) return HDP_ERR_INVALID_ARG;
+    if (Lk > 0 && (!k_chunk || !v_chunk)) return HDP_ERR_INVALID_ARG;
+    DeviceState* st = nullptr;
+    if (int rc = device_state(&st)) return rc;
+    hdp::FwdArgs a{};
+    a.q = (const uint16_t*)q_slice;
+    a.k = (const uint16_t*)k_chunk;
+    a.v = (const uint16_t*)v_chunk;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.scale_log2 = scale * kLog2e;
+    a.out = o_partial;
+    a.lse = lse;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    a.q_offset = q_offset;
+    a.kv_offset = kv_offset;
+    a.causal = causal ? 1 : 0;
+    int grid = 0;
+    schedule(st, H, Hkv, a, grid);
+    return hdp::launch_fwd_chunk(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+int hdp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,
+                  int32_t L, int32_t H, int32_t D, void* out_bf16, hipStream_t stream) {
+    if (L < 0 || H <= 0 || D <= 0) return HDP_ERR_INVALID_ARG;
+    if (!head_dim_ok(D)) return HDP_ERR_UNSUPPORTED;
+    if (L == 0) return HDP_OK;
+    if (!o_acc || !lse_acc || !o_part || !lse_part) return HDP_ERR_INVALID_ARG;
+    const int64_t rows = (int64_t)L * H;
+    if (rows / (256 / (D / 4)) + 1 > INT32_MAX) return HDP_ERR_OVERFLOW;
+    hdp::MergeArgs a{};
+    a.o_acc = o_acc;
+    a.lse_acc = lse_acc;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.out_bf16 = (uint16_t*)out_bf16;
+    a.rows = rows;
+    a.D = D;
+    return hdp::launch_lse_merge(a, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const float* lse, const void* dout, const int32_t* cu_seqlens,
+                        int32_t n_seq, int32_t T, int32_t H, int32_t Hkv, int32_t D,
+                        float scale, void* dq, void* dk, void* dv, hipStream_t stream) {
+    if (n_seq < 0 || T < 0) return HDP_ERR_INVALID_ARG;
+    if (int st = check_heads(H, Hkv, D)) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (n_seq == 0 || T == 0) return HDP_OK;
+    if (!q || !k || !v || !out || !lse || !dout || !cu_seqlens || !dq || !dk || !dv)
+        return HDP_ERR_INVALID_ARG;
+    (void)stream;
+    return HDP_ERR_UNSUPPORTED;
+}
+
+int hdp_release_workspace(void) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return HDP_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto itr = g_dev.find(dev);
+    if (itr == g_dev.end()) return HDP_OK;
+    if (hipDeviceSynchronize() != hipSuccess) return HDP_ERR_HIP;
+    if (itr->second.ws) (void)hipFree(itr->second.ws);
+    if (itr->second.counters) (void)hipFree(itr->second.counters);
+    g_dev.erase(itr);
+    return HDP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace hdp {
+
+// Work-queue counters: one per XCD queue plus a completion counter, each on its own 128-byte
+// line.  The last workgroup of a launch resets them, so they are zero between launches.
+constexpr int kQueueStride = 32;                 // ints between counters
+constexpr int kMaxQueues = 8;                    // one queue per XCD
+constexpr int kCounterInts = (kMaxQueues + 1) * kQueueStride;
+
+struct FwdArgs {
+    const uint16_t* q;      // [rows][H][D] bf16
+    const uint16_t* k;      // [keys][Hkv][D] bf16
+    const uint16_t* v;
+    const int32_t* cu;      // varlen: n_seq + 1 entries (device); chunk mode: unused
+    int32_t n_seq;
+    int32_t H, Hkv;
+    float scale_log2;       // scale * log2(e)
+    void* out;              // varlen: bf16 [T][H][D]; chunk: fp32 [Lq][H][D]
+    float* lse;             // [rows][H]
+    // chunk mode
+    int32_t Lq, Lk;
+    int64_t q_offset, kv_offset;
+    int32_t causal;
+    // scheduling
+    int* counters;          // kCounterInts ints, zero on entry
+    int32_t hpw;            // query heads per workgroup item (1, 2 or 4)
+    int32_t nqueues;        // 8 (one per XCD) or 1
+};
+
+struct F32Args {
+    const float* q;
+    const float* k;
+    const float* v;
+    const int32_t* cu;
+    int32_t n_seq;
+    int32_t H, Hkv, D;
+    float scale_log2;
+    float* out;
+    float* lse;
+};
+
+struct MergeArgs {
+    float* o_acc;
+    float* lse_acc;
+    const float* o_part;
+    const float* lse_part;
+    uint16_t* out_bf16;     // may be null
+    int64_t rows;           // L * H
+    int32_t D;
+};
+
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;
+    const float* lse;
+    const uint16_t* dout;
+    const int32_t* cu;
+    int32_t n_seq;
+    int32_t H, Hkv;
+    float scale;
+    float scale_log2;
+    float* delta;           // [T][H] workspace
+    float* dq_acc;          // [T][H][D] fp32 workspace
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    int* counters;
+    int32_t hpw;
+    int32_t nqueues;
+};
+
+// Launchers (return hipSuccess or the launch error).  `grid` is the persistent grid size.
+hipError_t launch_fwd_varlen(const FwdArgs& a, int D, int grid, hipStream_t s);
+hipError_t launch_fwd_chunk(const FwdArgs& a, int D, int grid, hipStream_t s);
+hipError_t launch_fwd_f32(const F32Args& a, hipStream_t s);
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int D, int grid, int64_t T_upper, hipStream_t s);
+
+// Upper bound on the rows a varlen call can touch, unknown on the host; the backward's
+// preprocess walks sequences on the device instead.
+}  // namespace hdp

@@ -1,0 +1,154 @@
+"""Python face of the C ABI: the same call names, torch tensors in, torch tensors out.
+
+PyTorch provides device memory and the current HIP stream; every step of the computation runs
+in libhdpattn.so.  Outputs not supplied by the caller are allocated here with torch.empty.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+PASS_FWD, PASS_BWD, PASS_FWD_BWD = 0, 1, 2
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _scale(D: int, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def hdp_attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None
+                        ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Packed causal varlen attention, bf16.  q [T,H,D], k/v [T,Hkv,D], cu_seqlens int32 [n+1]."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _dev_tensor("out", out, torch.bfloat16, 3)
+    _dev_tensor("lse", lse, torch.float32, 2)
+    st = _lib.lib().hdp_attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                        cu_seqlens.numel() - 1, H, Hkv, D, _scale(D, scale),
+                                        _ptr(out), _ptr(lse), _stream())
+    _lib.check("hdp_attn_varlen_fwd", st)
+    return out, lse
+
+
+def hdp_attn_varlen_fwd_f32(q, k, v, cu_seqlens, scale=None, out=None, lse=None
+                            ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp32 form of hdp_attn_varlen_fwd."""
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.float32, 3)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _dev_tensor("out", out, torch.float32, 3)
+    _dev_tensor("lse", lse, torch.float32, 2)
+    st = _lib.lib().hdp_attn_varlen_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
+                                            cu_seqlens.numel() - 1, H, Hkv, D, _scale(D, scale),
+                                            _ptr(out), _ptr(lse), _stream())
+    _lib.check("hdp_attn_varlen_fwd_f32", st)
+    return out, lse
+
+
+def hdp_attn_chunk_partial(q_slice, k_chunk, v_chunk, q_offset: int, kv_offset: int,
+                           causal: bool = True, scale=None, o_partial=None, lse=None
+                           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One ring step: q_slice [Lq,H,D] vs k/v chunk [Lk,Hkv,D] at global offsets (fp32 out)."""
+    for n, t in (("q_slice", q_slice), ("k_chunk", k_chunk), ("v_chunk", v_chunk)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    Lq, H, D = q_slice.shape
+    Lk, Hkv = k_chunk.shape[0], k_chunk.shape[1]
+    if o_partial is None:
+        o_partial = torch.empty((Lq, H, D), dtype=torch.float32, device=q_slice.device)
+    if lse is None:
+        lse = torch.empty((Lq, H), dtype=torch.float32, device=q_slice.device)
+    _dev_tensor("o_partial", o_partial, torch.float32, 3)
+    _dev_tensor("lse", lse, torch.float32, 2)
+    st = _lib.lib().hdp_attn_chunk_partial(_ptr(q_slice), Lq, _ptr(k_chunk), _ptr(v_chunk), Lk,
+                                           int(q_offset), int(kv_offset), int(bool(causal)), H,
+                                           Hkv, D, _scale(D, scale), _ptr(o_partial), _ptr(lse),
+                                           _stream())
+    _lib.check("hdp_attn_chunk_partial", st)
+    return o_partial, lse
+
+
+def hdp_lse_merge(o_acc, lse_acc, o_part, lse_part, out_bf16=None) -> None:
+    """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
+    _dev_tensor("o_acc", o_acc, torch.float32, 3)
+    _dev_tensor("lse_acc", lse_acc, torch.float32, 2)
+    _dev_tensor("o_part", o_part, torch.float32, 3)
+    _dev_tensor("lse_part", lse_part, torch.float32, 2)
+    L, H, D = o_acc.shape
+    if out_bf16 is not None:
+        _dev_tensor("out_bf16", out_bf16, torch.bfloat16, 3)
+    st = _lib.lib().hdp_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), L, H,
+                                  D, _ptr(out_bf16), _stream())
+    _lib.check("hdp_lse_merge", st)
+
+
+def hdp_attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None, dq=None, dk=None,
+                        dv=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of hdp_attn_varlen_fwd; returns (dq, dk, dv) in bf16."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("lse", lse, torch.float32, 2)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32, 1)
+    T, H, D = q.shape
+    Hkv = k.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    st = _lib.lib().hdp_attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        _ptr(dout), _ptr(cu_seqlens), cu_seqlens.numel() - 1, T,
+                                        H, Hkv, D, _scale(D, scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        _stream())
+    _lib.check("hdp_attn_varlen_bwd", st)
+    return dq, dk, dv
+
+
+def hdp_seq_flops(s: int, H: int, D: int, causal: bool = True, pass_: int = PASS_FWD) -> int:
+    return int(_lib.lib().hdp_seq_flops(int(s), int(H), int(D), int(bool(causal)), int(pass_)))
+
+
+def hdp_chunk_flops(Lq: int, Lk: int, q_offset: int, kv_offset: int, causal: bool, H: int,
+                    D: int, pass_: int = PASS_FWD) -> int:
+    return int(_lib.lib().hdp_chunk_flops(int(Lq), int(Lk), int(q_offset), int(kv_offset),
+                                          int(bool(causal)), int(H), int(D), int(pass_)))
+
+
+def hdp_release_workspace() -> None:
+    _lib.check("hdp_release_workspace", _lib.lib().hdp_release_workspace())
