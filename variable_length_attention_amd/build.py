@@ -17,6 +17,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are kept out of the device code on purpose.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # MFMA accumulators in VGPRs: the online-softmax rescale touches the output
+                # accumulator with VALU ops, and AGPR accumulators would be copied every step.
+                "-mllvm", "-amdgpu-mfma-vgpr-form",
                 "-I", INCLUDE, "-I", CSRC]
 
 

@@ -213,6 +213,7 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
     if (int st = check_heads(H, Hkv, D)) return st;
     if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
     if (q_offset > INT64_MAX / 4 || kv_offset > INT64_MAX / 4) return HDP_ERR_OVERFLOW;
+    if (Lq > (1 << 30) || Lk > (1 << 30)) return HDP_ERR_OVERFLOW;
     if (Lq == 0) return HDP_OK;
     if (!q_slice || !o_partial || !lse) return HDP_ERR_INVALID_ARG;
     if (Lk > 0 && (!k_chunk || !v_chunk)) return HDP_ERR_INVALID_ARG;
@@ -229,8 +230,10 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
     a.lse = lse;
     a.Lq = Lq;
     a.Lk = Lk;
-    a.q_offset = q_offset;
-    a.kv_offset = kv_offset;
+    // Key j is visible to row r iff j <= (q_offset - kv_offset) + r; for 0 <= j < Lk and
+    // 0 <= r < Lq that only depends on the difference clamped to [-Lq, Lk].
+    const int64_t d = q_offset - kv_offset;
+    a.delta = (int32_t)std::max<int64_t>(-(int64_t)Lq, std::min<int64_t>(d, Lk));
     a.causal = causal ? 1 : 0;
     int grid = 0;
     schedule(st, H, Hkv, a, grid);

@@ -15,9 +15,17 @@
 //     O^T (D x rows)   += V^T (D x keys) * P^T (keys x rows)
 // In this orientation every lane holds whole query rows, so the row max and row sum are
 // in-lane reductions plus one swap between the two half-waves, and the softmax output P^T is
-// already in the B-operand layout of the second product.  V^T is read from row-major LDS with
-// the gfx950 transposing read ds_read_b64_tr_b16.  K and V tiles of 64 keys are double
-// buffered in LDS; the next tile's global loads are in flight while the current one computes.
+// already in the B-operand layout of the second product.  Holding 64 rows per wave lets each
+// K or V fragment read from LDS feed two MFMAs, which keeps LDS traffic at half the rate the
+// matrix cores consume.  V^T is read from row-major LDS with the gfx950 transposing read
+// ds_read_b64_tr_b16.
+//
+// Pipeline.  Keys are processed in units of 32.  Iteration u issues the value product of unit
+// u-1 and the score product of unit u+1 on the matrix cores and runs the softmax of unit u on
+// the vector ALUs; the three are independent.  K/V arrive in stages of 64 keys through direct
+// global->LDS loads (global_load_lds_dwordx4, no registers), three stages deep, one workgroup
+// barrier per stage.  LDS rows are unpadded and their 16-byte slots are XOR-swizzled by the
+// row index, so the rows a fragment read touches fall on different banks.
 //
 // Softmax uses exp2 with scale*log2(e) folded into one FMA, and a lazy running max: the
 // accumulator is rescaled only when some row's max grows by more than 2^8, which keeps every
@@ -31,42 +39,42 @@
 // queue per XCD and head block b is served only by the XCD b mod 8, so each K/V head's tiles
 // stay in one XCD's L2.  The order is decoded on the device from cu_seqlens, without a
 // planning launch.
+#include <type_traits>
+
 #include "hdp_internal.h"
 
 namespace hdp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 64;      // two 32-row MFMA column tiles
 constexpr int kNT = 2;
-constexpr int kBN = 64;               // keys per LDS stage: two 32-key MFMA row tiles
+constexpr int kItemRowHeads = 256;    // query (row, head) pairs per item
+constexpr int kUnit = 32;             // keys per pipeline step
+constexpr int kStage = 64;            // keys per LDS stage
+constexpr int kStages = 3;            // LDS ring depth
 constexpr float kLazy = 8.0f;         // rescale threshold, log2 units
 constexpr float kLn2 = 0.693147180559945309f;
 
 template <int D>
 struct Cfg {
-    static constexpr int kPitch = D + 8;                   // bf16 per LDS row (16-byte pad)
-    static constexpr int kTile = kBN * kPitch;             // bf16 per K or V stage
-    static constexpr int kChunks = D / 8;                  // 16-byte chunks per key row
-    static constexpr int kLoads = kBN * kChunks / kThreads;
-    static constexpr int kKS = D / 16;                     // k-steps of the score product
-    static constexpr int kMT = D / 32;                     // D tiles of the value product
-};
-
-struct Item {
-    int64_t qbase;   // packed row of query position 0
-    int64_t kbase;   // packed row of key position 0
-    int32_t s;       // query rows
-    int32_t sk;      // keys
-    int32_t hb;      // head block
-    int32_t tg;      // query tile group
+    static constexpr int kRowBytes = D * 2;                       // unpadded bf16 row
+    static constexpr int kTileBytes = kStage * kRowBytes;         // one K or V stage
+    static constexpr int kChunks = D / 8;                         // 16-byte chunks per row
+    static constexpr int kRowsPerBlock = 64 / kChunks;            // rows per 1 KB wave load
+    static constexpr int kBlocksPerWave = kStage / kRowsPerBlock / kWaves;
+    static constexpr int kKS = D / 16;                            // k-steps, score product
+    static constexpr int kMT = D / 32;                            // D tiles, value product
 };
 
 __device__ inline float xhalf_max(float x) {
@@ -113,11 +121,11 @@ __device__ int levels_above(const int32_t* cu, int n_seq, int Tc, int W, int c, 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][C::kTile];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][C::kTileBytes];
     __shared__ int s_item[8];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
@@ -125,14 +133,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     const int H = args.H, Hkv = args.Hkv;
     const int G = H / Hkv;
     const int hpw = args.hpw;
-    const int qpw = 4 / hpw;
-    const int W = kRowsPerWave * qpw;          // query rows per item
+    const int W = kItemRowHeads / hpw;         // query rows per item
     const int nhb = H / hpw;
     const int nq_queues = args.nqueues;
     const int queue = blockIdx.x % nq_queues;
     const int nhbq = nhb / nq_queues;          // head blocks per queue
     const int64_t q_stride = (int64_t)H * D;
     const int64_t kv_stride = (int64_t)Hkv * D;
+    const float c2 = args.scale_log2;
 
     // ---- per-launch totals (wave 0 only) ----
     int total = 0, maxc = 0, Tc = 0;
@@ -153,6 +161,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             total = ((args.Lq + W - 1) / W) * nhbq;
         }
     }
+
+    // per-lane constants of the fragment reads
+    const int gidx = lane >> 4;                                   // 16-lane group (V^T reads)
+    const int tr_row = 4 * (gidx >> 1) + ((lane & 15) >> 2);
+    const int tr_col = 16 * (gidx & 1) + 4 * (lane & 3);          // bf16 column within 32
+    const int tr_sub = (lane & 1) * 8;                            // byte offset within a slot
 
     for (;;) {
         // ---- pop and decode the next item (wave 0) ----
@@ -214,200 +228,188 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
         }
         __syncthreads();
-        if (s_item[0] < 0) break;
-        Item it;
-        it.qbase = s_item[0];
-        it.kbase = MODE == 0 ? it.qbase : 0;
-        it.s = s_item[1];
-        it.sk = MODE == 0 ? it.s : args.Lk;
-        it.hb = s_item[2];
-        it.tg = s_item[3];
-        const int64_t qpos0 = MODE == 0 ? 0 : args.q_offset;
-        const int64_t kpos0 = MODE == 0 ? 0 : args.kv_offset;
+        // item fields are uniform: keep them in scalar registers
+        const int it_a = __builtin_amdgcn_readfirstlane(s_item[0]);
+        if (it_a < 0) break;
+        const int64_t qbase = it_a;
+        const int64_t kbase = MODE == 0 ? qbase : 0;
+        const int s_rows = __builtin_amdgcn_readfirstlane(s_item[1]);
+        const int sk = MODE == 0 ? s_rows : args.Lk;
+        const int hb = __builtin_amdgcn_readfirstlane(s_item[2]);
+        const int tg = __builtin_amdgcn_readfirstlane(s_item[3]);
+        // query position minus key position of (row 0, key 0)
+        const int delta = MODE == 0 ? 0 : args.delta;
         const bool causal = MODE == 0 ? true : (args.causal != 0);
 
-        const int head = it.hb * hpw + (wave % hpw);
-        const int g = (it.hb * hpw) / G;
-        const int t = it.tg * qpw + wave / hpw;       // this wave's query tile
-        const int r_lo = t * kRowsPerWave;
-        const int r_hi = min(r_lo + kRowsPerWave, it.s) - 1;
-        const bool wave_rows = r_lo < it.s;
-        // key tiles the workgroup visits
-        const int wg_rmax = min(it.s, (it.tg + 1) * W) - 1;
-        int64_t jmax = it.sk - 1;
-        if (causal) jmax = min(jmax, qpos0 + wg_rmax - kpos0);
-        const int n_tiles = (wg_rmax < 0 || jmax < 0) ? 0 : (int)(jmax / kBN) + 1;
+        const int head = hb * hpw + (wave % hpw);
+        const int g = (hb * hpw) / G;
+        const int r_lo = tg * W + (wave / hpw) * kRowsPerWave;   // this wave's first row
+        const bool wave_rows = r_lo < s_rows;
+        // keys the workgroup visits
+        const int wg_rmax = min(s_rows, (tg + 1) * W) - 1;
+        int jmax = sk - 1;
+        if (causal) jmax = min(jmax, delta + wg_rmax);
+        const int n_units = (wg_rmax < 0 || jmax < 0) ? 0 : (int)(jmax / kUnit) + 1;
+        const int n_stages = (n_units + 1) / 2;
 
         // ---- Q^T fragments in registers ----
         u32x4 qf[kNT][C::kKS];
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             const int row = r_lo + nt * 32 + l32;
-            const bool ok = row < it.s;
-            const uint16_t* qp = args.q + (it.qbase + row) * q_stride + (int64_t)head * D + half * 8;
+            const bool ok = row < s_rows;
+            const uint16_t* qp = args.q + (qbase + row) * q_stride + (int64_t)head * D + half * 8;
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks)
                 qf[nt][ks] = ok ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
         }
 
-        f32x16 o[C::kMT][kNT];
+        // Per-row visibility limit: key j (relative to key 0) is visible to this lane's row of
+        // column tile nt iff j <= lim0[nt] (causal) and j < sk.
+        int lim0[kNT];
 #pragma unroll
-        for (int mt = 0; mt < C::kMT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) o[mt][nt] = f32x16{};
-        float m[kNT], l[kNT];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; l[nt] = 0.f; }
+        for (int nt = 0; nt < kNT; ++nt)
+            lim0[nt] = causal ? delta + r_lo + nt * 32 + l32 : sk - 1;
 
-        // ---- K/V tile staging ----
-        u32x4 kreg[C::kLoads], vreg[C::kLoads];
-        auto load_tile = [&](int jt) {
+        // ---- direct global -> LDS stage loads (K and V of 64 keys) ----
+        auto load_stage = [&](int st) {
+            unsigned char* kb = smem[st % kStages][0];
+            unsigned char* vb = smem[st % kStages][1];
 #pragma unroll
-            for (int u = 0; u < C::kLoads; ++u) {
-                const int c = tid + u * kThreads;
-                const int key = c / C::kChunks, part = c % C::kChunks;
-                const int j = jt * kBN + key;
-                if (j < it.sk) {
-                    const int64_t off = (it.kbase + j) * kv_stride + (int64_t)g * D + part * 8;
-                    kreg[u] = *(const u32x4*)(args.k + off);
-                    vreg[u] = *(const u32x4*)(args.v + off);
-                } else {
-                    kreg[u] = u32x4{0, 0, 0, 0};
-                    vreg[u] = u32x4{0, 0, 0, 0};
-                }
-            }
-        };
-        auto store_tile = [&](int buf) {
-#pragma unroll
-            for (int u = 0; u < C::kLoads; ++u) {
-                const int c = tid + u * kThreads;
-                const int key = c / C::kChunks, part = c % C::kChunks;
-                *(u32x4*)&smem[buf][0][key * C::kPitch + part * 8] = kreg[u];
-                *(u32x4*)&smem[buf][1][key * C::kPitch + part * 8] = vreg[u];
+            for (int i = 0; i < C::kBlocksPerWave; ++i) {
+                const int blk = wave * C::kBlocksPerWave + i;
+                const int row = blk * C::kRowsPerBlock + lane / C::kChunks;
+                const int slot = lane % C::kChunks;
+                const int chunk = slot ^ (row & 7);
+                const int j = min(st * kStage + row, sk - 1);    // clamp into this sequence
+                const int64_t off = (kbase + j) * kv_stride + (int64_t)g * D + chunk * 8;
+                __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
             }
         };
 
-        if (n_tiles > 0) {
-            load_tile(0);
-            store_tile(0);
-        }
-        __syncthreads();
-
-        // per-lane constant parts of the transposing V reads
-        const int gidx = lane >> 4;                  // 16-lane group
-        const int tr_row = 4 * (gidx >> 1) + ((lane & 15) >> 2);
-        const int tr_col = 16 * (gidx & 1) + 4 * (lane & 3);
-
-        for (int jt = 0; jt < n_tiles; ++jt) {
-            const int buf = jt & 1;
-            if (jt + 1 < n_tiles) load_tile(jt + 1);
-            const int64_t j0 = (int64_t)jt * kBN;
-            bool active = wave_rows;
-            if (causal && kpos0 + j0 > qpos0 + r_hi) active = false;
-            if (active) {
-                const uint16_t* Ks = smem[buf][0];
-                const uint16_t* Vs = smem[buf][1];
-                // Two 32-key sub-tiles per stage; each runs score, softmax and value products.
+        // K fragments of unit u (A operand of the score product), read from LDS
+        auto read_k = [&](int u, u32x4 (&kf)[C::kKS]) {
+            const unsigned char* kb = smem[(u >> 1) % kStages][0];
+            const int row = (u & 1) * 32 + l32;
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    const int64_t js = j0 + kt * 32;
-                    if (causal && kpos0 + js > qpos0 + r_hi) continue;
-                    const bool full = (js + 31 < it.sk) && (!causal || kpos0 + js + 31 <= qpos0 + r_lo);
-                    // S^T = K Q^T
-                    f32x16 sacc[kNT];
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) sacc[nt] = f32x16{};
-#pragma unroll
-                    for (int ks = 0; ks < C::kKS; ++ks) {
-                        const u32x4 araw = *(const u32x4*)&Ks[(kt * 32 + l32) * C::kPitch + ks * 16 + half * 8];
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, araw);
-#pragma unroll
-                        for (int nt = 0; nt < kNT; ++nt)
-                            sacc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                a, __builtin_bit_cast(bf16x8, qf[nt][ks]), sacc[nt], 0, 0, 0);
-                    }
-                    if (!full) {
-#pragma unroll
-                        for (int nt = 0; nt < kNT; ++nt) {
-                            const int64_t qpos = qpos0 + r_lo + nt * 32 + l32;
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) {
-                                const int64_t j = js + 8 * (i >> 2) + 4 * half + (i & 3);
-                                const bool vis = j < it.sk && (!causal || kpos0 + j <= qpos);
-                                if (!vis) sacc[nt][i] = -INFINITY;
-                            }
-                        }
-                    }
-                    // online softmax (rows live in lanes)
-                    float tmax[kNT];
-                    bool need = false;
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) {
-                        float mx = -INFINITY;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nt][i]);
-                        mx = xhalf_max(mx);
-                        tmax[nt] = mx * args.scale_log2;
-                        need |= tmax[nt] > m[nt] + kLazy;
-                    }
-                    if (__ballot(need)) {
-#pragma unroll
-                        for (int nt = 0; nt < kNT; ++nt) {
-                            const float mn = fmaxf(m[nt], tmax[nt]);
-                            const float alpha = (m[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mn);
-                            m[nt] = mn;
-                            l[nt] *= alpha;
-#pragma unroll
-                            for (int mt = 0; mt < C::kMT; ++mt) o[mt][nt] *= alpha;
-                        }
-                    }
-                    bf16x8 pb[kNT][2];
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) {
-                        const float mb = (m[nt] == -INFINITY) ? 0.f : m[nt];
-                        float ls = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[nt][i], args.scale_log2, -mb));
-                            ls += p;
-                            pb[nt][i >> 3][i & 7] = (__bf16)p;
-                        }
-                        l[nt] += ls;
-                    }
-                    // O^T += V^T P^T
-#pragma unroll
-                    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-                        for (int mt = 0; mt < C::kMT; ++mt) {
-                            const int row0 = kt * 32 + 16 * ks2 + tr_row;
-                            const uint16_t* p0 = &Vs[row0 * C::kPitch + mt * 32 + tr_col];
-                            const uint16_t* p1 = p0 + 8 * C::kPitch;
-                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-                            bf16x8 a;
-                            a.lo = __builtin_bit_cast(__bf16 __attribute__((ext_vector_type(4))), lo);
-                            a.hi = __builtin_bit_cast(__bf16 __attribute__((ext_vector_type(4))), hi);
-#pragma unroll
-                            for (int nt = 0; nt < kNT; ++nt)
-                                o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nt][ks2], o[mt][nt], 0, 0, 0);
-                        }
-                }
+            for (int ks = 0; ks < C::kKS; ++ks) {
+                const int slot = (2 * ks + half) ^ (row & 7);
+                kf[ks] = *(const u32x4*)(kb + row * C::kRowBytes + slot * 16);
             }
-            if (jt + 1 < n_tiles) store_tile(buf ^ 1);
-            __syncthreads();
-        }
-
-        // ---- epilogue ----
-        if (wave_rows) {
+        };
+        // V^T fragments of unit u (A operand of the value product), transposing LDS reads
+        auto read_v = [&](int u, bf16x8 (&vf)[2][C::kMT]) {
+            const unsigned char* vb = smem[(u >> 1) % kStages][1];
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt) {
+                    const int chunk = (mt * 32 + tr_col) >> 3;
+                    const int r0 = (u & 1) * 32 + 16 * ks2 + tr_row;
+                    const int r1 = r0 + 8;
+                    const unsigned char* p0 = vb + r0 * C::kRowBytes + ((chunk ^ (r0 & 7)) << 4) + tr_sub;
+                    const unsigned char* p1 = vb + r1 * C::kRowBytes + ((chunk ^ (r1 & 7)) << 4) + tr_sub;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+                    vf[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
+                    vf[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
+                }
+        };
+        // S^T (32 keys x 64 rows) = K Q^T
+        auto score = [&](const u32x4 (&kf)[C::kKS], f32x16 (&S)[kNT]) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) S[nt] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < C::kKS; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+                    S[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[nt][ks]), S[nt], 0, 0, 0);
+        };
+        // O^T += V^T P^T
+        auto value = [&](f32x16 (&oo)[C::kMT][kNT], const bf16x8 (&vf)[2][C::kMT], const bf16x8 (&P)[kNT][2]) {
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt)
+                        oo[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks2][mt], P[nt][ks2], oo[mt][nt], 0, 0, 0);
+        };
+        // mask of unit u (only units that reach past the diagonal or the last key)
+        // Key 8*(i/4) + 4*half + (i%4) of the unit is visible iff it is <= the row's limit; the
+        // half-wave term moves into the limit so the comparisons are against constants.
+        auto apply_mask = [&](int u, f32x16 (&S)[kNT]) {
+            const int j0 = u * kUnit;
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                const float lt = xhalf_sum(l[nt]);
+                const int lim = min(lim0[nt], sk - 1) - j0;
+                const int li = max(-1, min(lim, kUnit)) - 4 * half;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    S[nt][i] = (8 * (i >> 2) + (i & 3)) > li ? -INFINITY : S[nt][i];
+            }
+        };
+        auto unit_full = [&](int u) {
+            const int j0 = u * kUnit;
+            return (j0 + kUnit - 1 < sk) && (!causal || j0 + kUnit - 1 <= delta + r_lo);
+        };
+        // row max of a unit in log2 units (both half-waves)
+        auto row_max = [&](const f32x16 (&S)[kNT], float (&tmax)[kNT]) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                float mx = S[nt][0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[nt][i]);
+                tmax[nt] = xhalf_max(mx) * c2;
+            }
+        };
+        // P^T = exp2(S c2 - m) as bf16 B operands, row sums into ll
+        auto exponentials = [&](const f32x16 (&S)[kNT], const float (&mm)[kNT], float (&ll)[kNT], bf16x8 (&P)[kNT][2]) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const float mb = (mm[nt] == -INFINITY) ? 0.f : mm[nt];
+                float ls = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[nt][i], c2, -mb));
+                    ls += p;
+                    P[nt][i >> 3][i & 7] = (__bf16)p;
+                }
+                ll[nt] += ls;
+            }
+        };
+        // stage ring: at odd u, stage (u+3)/2 goes into the buffer of stage (u-3)/2 (last read
+        // in iteration u-1 or earlier); stage (u+1)/2, issued at u-2, must have landed.
+        auto stage_turn = [&](int u) {
+            if (u & 1) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                __syncthreads();
+                const int st = (u + 3) >> 1;
+                if (st < n_stages) load_stage(st);
+            }
+        };
+        auto stage_prologue = [&]() {
+            if (n_units > 0) {
+                load_stage(0);
+                if (n_stages > 1) load_stage(1);
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
+            __syncthreads();
+        };
+        // normalise and write this wave's rows
+        auto store_rows = [&](const f32x16 (&oo)[C::kMT][kNT], const float (&mm)[kNT], const float (&ll)[kNT]) {
+            if (!wave_rows) return;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const float lt = xhalf_sum(ll[nt]);
                 const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                const float mb = (m[nt] == -INFINITY) ? 0.f : m[nt];
+                const float mb = (mm[nt] == -INFINITY) ? 0.f : mm[nt];
                 const float lse = lt > 0.f ? (mb + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
                 const int row = r_lo + nt * 32 + l32;
-                if (row < it.s) {
-                    const int64_t orow = (it.qbase + row) * (int64_t)H + head;
+                if (row < s_rows) {
+                    const int64_t orow = (qbase + row) * (int64_t)H + head;
                     if (MODE == 0) {
                         uint16_t* op = (uint16_t*)args.out + orow * D;
 #pragma unroll
@@ -416,8 +418,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                             for (int a4 = 0; a4 < 4; ++a4) {
                                 const int d0 = mt * 32 + 8 * a4 + 4 * half;
                                 u32x2 w;
-                                w[0] = pack_bf16x2(o[mt][nt][4 * a4 + 0] * inv, o[mt][nt][4 * a4 + 1] * inv);
-                                w[1] = pack_bf16x2(o[mt][nt][4 * a4 + 2] * inv, o[mt][nt][4 * a4 + 3] * inv);
+                                w[0] = pack_bf16x2(oo[mt][nt][4 * a4 + 0] * inv, oo[mt][nt][4 * a4 + 1] * inv);
+                                w[1] = pack_bf16x2(oo[mt][nt][4 * a4 + 2] * inv, oo[mt][nt][4 * a4 + 3] * inv);
                                 *(u32x2*)(op + d0) = w;
                             }
                     } else {
@@ -427,15 +429,86 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
                             for (int a4 = 0; a4 < 4; ++a4) {
                                 const int d0 = mt * 32 + 8 * a4 + 4 * half;
-                                float4 w = make_float4(o[mt][nt][4 * a4 + 0] * inv, o[mt][nt][4 * a4 + 1] * inv,
-                                                       o[mt][nt][4 * a4 + 2] * inv, o[mt][nt][4 * a4 + 3] * inv);
+                                float4 w = make_float4(oo[mt][nt][4 * a4 + 0] * inv, oo[mt][nt][4 * a4 + 1] * inv,
+                                                       oo[mt][nt][4 * a4 + 2] * inv, oo[mt][nt][4 * a4 + 3] * inv);
                                 *(float4*)(op + d0) = w;
                             }
                     }
                     if (half == 0) args.lse[orow] = lse;
                 }
             }
+        };
+
+        // ---- software-pipelined units with a lazily rescaled running max ----
+        // Step u issues the value product of unit u-1 and the score product of unit u+1 and
+        // runs the softmax of unit u; the three are independent.  The running max is raised
+        // (and the accumulator rescaled) only when some row's max grows by more than 2^8, which
+        // keeps every P <= 256; numerator and denominator share the reference, so the result is
+        // exact whatever reference is used.
+        stage_prologue();
+        f32x16 o[C::kMT][kNT];
+#pragma unroll
+        for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) o[mt][nt] = f32x16{};
+        float m[kNT], l[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; l[nt] = 0.f; }
+
+        auto softmax_lazy = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2]) {
+            float tmax[kNT];
+            row_max(S, tmax);
+            bool need = false;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) need |= tmax[nt] > m[nt] + kLazy;
+            if (__ballot(need)) {
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    const float mn = fmaxf(m[nt], tmax[nt]);
+                    const float alpha = (m[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mn);
+                    m[nt] = mn;
+                    l[nt] *= alpha;
+#pragma unroll
+                    for (int mt = 0; mt < C::kMT; ++mt) o[mt][nt] *= alpha;
+                }
+            }
+            exponentials(S, m, l, P);
+        };
+
+        if (n_units > 0) {
+            f32x16 Sc[kNT], Sn[kNT];
+            bf16x8 Pp[kNT][2], Pc[kNT][2];
+            {
+                u32x4 kf[C::kKS];
+                read_k(0, kf);
+                score(kf, Sc);
+            }
+            for (int u = 0; u < n_units; ++u) {
+                stage_turn(u);
+                if (u >= 1) {
+                    bf16x8 vf[2][C::kMT];
+                    read_v(u - 1, vf);
+                    value(o, vf, Pp);
+                }
+                if (u + 1 < n_units) {
+                    u32x4 kf[C::kKS];
+                    read_k(u + 1, kf);
+                    score(kf, Sn);
+                }
+                if (!unit_full(u)) apply_mask(u, Sc);
+                softmax_lazy(Sc, Pc);
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    Sc[nt] = Sn[nt];
+                    Pp[nt][0] = Pc[nt][0];
+                    Pp[nt][1] = Pc[nt][1];
+                }
+            }
+            bf16x8 vf[2][C::kMT];
+            read_v(n_units - 1, vf);
+            value(o, vf, Pp);
         }
+        store_rows(o, m, l);
         __syncthreads();
     }
 

@@ -24,7 +24,7 @@ struct FwdArgs {
     float* lse;             // [rows][H]
     // chunk mode
     int32_t Lq, Lk;
-    int64_t q_offset, kv_offset;
+    int32_t delta;          // q_offset - kv_offset clamped to [-Lq, Lk] (same visibility)
     int32_t causal;
     // scheduling
     int* counters;          // kCounterInts ints, zero on entry
