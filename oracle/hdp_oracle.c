@@ -256,8 +256,9 @@ int orc_varlen_bwd(const double* q, const double* k, const double* v, const doub
     for (int64_t i = 0; i < n_seq; ++i)
         if (cu[i + 1] - cu[i] > max_len) max_len = cu[i + 1] - cu[i];
 
-    /* Step 1: which sequences own a requested row. */
-    unsigned char* need = (unsigned char*)calloc((size_t)(n_seq + 1), 1);
+    /* Step 1: the rows whose lse and delta the requested outputs use: each dq row itself, and
+     * for a dk/dv row t every row of its sequence from t to the end (the rows that see key t). */
+    unsigned char* need = (unsigned char*)calloc((size_t)(T + 1), 1);
     double* lse = (double*)malloc(sizeof(double) * (size_t)(T * H + 1));
     double* delta = (double*)malloc(sizeof(double) * (size_t)(T * H + 1));
     if (!need || !lse || !delta) {
@@ -265,12 +266,14 @@ int orc_varlen_bwd(const double* q, const double* k, const double* v, const doub
         return ORC_NO_MEM;
     }
     for (int64_t n = 0; n < n_q; ++n) {
-        int64_t s = owner_seq(cu, n_seq, qrows ? qrows[n] : n);
-        if (s >= 0) need[s] = 1;
+        const int64_t t = qrows ? qrows[n] : n;
+        if (owner_seq(cu, n_seq, t) >= 0) need[t] = 1;
     }
     for (int64_t n = 0; n < n_k; ++n) {
-        int64_t s = owner_seq(cu, n_seq, krows ? krows[n] : n);
-        if (s >= 0) need[s] = 1;
+        const int64_t t = krows ? krows[n] : n;
+        const int64_t s = owner_seq(cu, n_seq, t);
+        if (s >= 0)
+            for (int64_t u = t; u < cu[s + 1]; ++u) need[u] = 1;
     }
     int status = ORC_OK;
     set_threads(nthreads);
@@ -287,8 +290,9 @@ int orc_varlen_bwd(const double* q, const double* k, const double* v, const doub
         } else {
 #pragma omp for schedule(dynamic, 4)
             for (int64_t t = 0; t < T; ++t) {
+                if (!need[t]) continue;
                 const int64_t s = owner_seq(cu, n_seq, t);
-                if (s < 0 || !need[s]) continue;
+                if (s < 0) continue;
                 const int64_t a = cu[s], r = t - a;
                 for (int64_t j = 0; j <= r; ++j) vis[j] = 1;
                 for (int h = 0; h < H; ++h) {

@@ -40,3 +40,24 @@ def lse_close(gpu_lse, ref: np.ndarray, tol: float) -> float:
     err = float(np.max(d)) if d.size else 0.0
     assert err <= tol, err
     return err
+
+
+def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 numbers at |ref| (8 significand bits): the rounding any bf16
+    result of ref must carry, on top of the arithmetic error."""
+    a = np.abs(ref)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 8), 0.0)
+
+
+def grad_close(gpu_t, ref: np.ndarray, tol: float = TOL_BF16_OUT, mean_tol: float = 2e-3):
+    """bf16 gradient check: |gpu - ref| <= tol + half a bf16 ulp of ref everywhere, and the mean
+    error stays small.  Returns (max error, max error beyond the half ulp, mean error)."""
+    g = gpu_t.detach().float().cpu().double().numpy()
+    err = np.abs(g - ref)
+    over = err - bf16_half_ulp(ref)
+    worst = float(np.max(over)) if over.size else 0.0
+    mean = float(np.mean(err)) if err.size else 0.0
+    assert worst <= tol, (float(np.max(err)), worst)
+    assert mean <= mean_tol, mean
+    return float(np.max(err)) if err.size else 0.0, worst, mean

@@ -1,0 +1,109 @@
+"""GPU parity of the backward pass against the fp64 oracle, through the C ABI.
+
+Tolerance: gradients are bf16 results, and a bf16 number is within half its ulp of the exact
+value at best; gradient magnitudes reach 8-16 here, where that half ulp (0.03) alone exceeds
+2e-2.  So each element must satisfy |gpu - oracle| <= 2e-2 + half a bf16 ulp of the oracle
+value, and the mean error must stay below 2e-3.
+
+The GPU backward consumes the GPU forward's out and lse (as a training step would); the oracle
+differentiates its own fp64 forward.  Small packs compare every element of dq, dk and dv; the
+full-size workloads compare sampled rows the oracle evaluates one by one (dq rows anywhere,
+dk/dv rows where the rows that see them are few enough to evaluate).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import grad_close, to_gpu
+from variable_length_attention_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(w, q, k, v, do, cu):
+    qg, kg, vg, dog = to_gpu(q, k, v, do)
+    cug = torch.from_numpy(cu).cuda()
+    out, lse = ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale)
+    dq, dk, dv = ops.hdp_attn_varlen_bwd(qg, kg, vg, out, lse, dog, cug, w.scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def case(lengths, H, Hkv, D, seed):
+    w = synth.Workload("case", "varlen", H, Hkv, D, "bf16", list(lengths), seed)
+    q, k, v, do = synth.varlen_tensors(w, with_dout=True)
+    return w, q, k, v, do, synth.cu_seqlens(w.lengths)
+
+
+@pytest.mark.parametrize("lengths,H,Hkv,D", [
+    ([1, 17, 64, 65, 127, 200, 0, 33], 32, 8, 128),
+    ([100, 3, 129], 8, 8, 64),
+    ([70, 31, 160], 4, 2, 128),
+    ([45, 90], 16, 2, 64),
+    ([300], 6, 2, 128),
+])
+def test_backward_small_packs_full(lengths, H, Hkv, D):
+    w, q, k, v, do, cu = case(lengths, H, Hkv, D, seed=40)
+    dq, dk, dv = run_fwd_bwd(w, q, k, v, do, cu)
+    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, w.scale)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        e = grad_close(g, r)
+        print("lengths=%s H=%d Hkv=%d D=%d %s: max %.3g, beyond half-ulp %.3g, mean %.2g"
+              % (lengths, H, Hkv, D, name, *e))
+
+
+def test_backward_is_deterministic_and_isolated_per_sequence():
+    lengths = [150, 64, 257]
+    w, q, k, v, do, cu = case(lengths, 32, 8, 128, seed=41)
+    a = run_fwd_bwd(w, q, k, v, do, cu)
+    b = run_fwd_bwd(w, q, k, v, do, cu)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    # change the middle sequence: gradients of the other two are bit-identical
+    s0, s1 = int(cu[1]), int(cu[2])
+    q2, k2, v2, do2 = q.clone(), k.clone(), v.clone(), do.clone()
+    q2[s0:s1] *= 2
+    v2[s0:s1] = -v2[s0:s1]
+    do2[s0:s1] += 1
+    c = run_fwd_bwd(w, q2, k2, v2, do2, cu)
+    keep = torch.ones(int(cu[-1]), dtype=torch.bool)
+    keep[s0:s1] = False
+    keep = keep.cuda()
+    for x, y in zip(a, c):
+        assert torch.equal(x[keep].view(torch.int16), y[keep].view(torch.int16))
+
+
+def tail_key_rows(cu, per_seq=(0, 1, 7, 63, 200), long_cut=1200):
+    """Key rows whose gradient needs few rows: near each sequence's end, plus the first key of
+    the shorter sequences."""
+    rows = set()
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        for d in per_seq:
+            if b - 1 - d >= a:
+                rows.add(b - 1 - d)
+        if 0 < b - a <= long_cut:
+            rows.add(a)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("make", [synth.fwd_bwd_8k_slice, synth.fwd_bwd_8k_single])
+def test_backward_full_size_sampled(make):
+    w = make()
+    q, k, v, do = synth.varlen_tensors(w, with_dout=True)
+    cu = synth.cu_seqlens(w.lengths)
+    dq, dk, dv = run_fwd_bwd(w, q, k, v, do, cu)
+    T = int(cu[-1])
+    qrows = np.unique(np.concatenate([np.arange(0, T, 97), cu[:-1], cu[1:] - 1]))
+    qrows = qrows[(qrows >= 0) & (qrows < T)]
+    krows = tail_key_rows(cu)
+    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, w.scale, qrows=qrows, krows=krows)
+    iq = torch.from_numpy(qrows).cuda()
+    ik = torch.from_numpy(krows).cuda()
+    for name, g, r in (("dq", dq[iq], rq), ("dk", dk[ik], rk), ("dv", dv[ik], rv)):
+        e = grad_close(g, r)
+        print("%s %s (%d dq rows, %d dk/dv rows): max %.3g, beyond half-ulp %.3g, mean %.2g"
+              % (w.name, name, len(qrows), len(krows), *e))
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()

@@ -269,8 +269,36 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     if (n_seq == 0 || T == 0) return HDP_OK;
     if (!q || !k || !v || !out || !lse || !dout || !cu_seqlens || !dq || !dk || !dv)
         return HDP_ERR_INVALID_ARG;
-    (void)stream;
-    return HDP_ERR_UNSUPPORTED;
+    if ((int64_t)T * H > (int64_t)INT32_MAX) return HDP_ERR_OVERFLOW;
+    DeviceState* st = nullptr;
+    if (int rc = device_state(&st)) return rc;
+    if (int rc = ensure_workspace(st, sizeof(float) * (size_t)T * (size_t)H)) return rc;
+    hdp::BwdArgs a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.out = (const uint16_t*)out;
+    a.lse = lse;
+    a.dout = (const uint16_t*)dout;
+    a.cu = cu_seqlens;
+    a.n_seq = n_seq;
+    a.T = T;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.scale = scale;
+    a.scale_log2 = scale * kLog2e;
+    a.delta = (float*)st->ws;
+    a.dq = (uint16_t*)dq;
+    a.dk = (uint16_t*)dk;
+    a.dv = (uint16_t*)dv;
+    a.counters = st->counters;
+    a.hpw = heads_per_item(H, Hkv);
+    const int grid = st->cus;
+    const bool q8 = (H / a.hpw) % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
+    const bool kv8 = Hkv % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
+    a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
+    a.nqueues_kv = kv8 ? hdp::kMaxQueues : 1;
+    return hdp::launch_bwd(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 
 int hdp_release_workspace(void) {

@@ -1,0 +1,151 @@
+// Device helpers shared by the attention kernels: vector types, wave reductions, bf16 packing
+// and the longest-first work queue over (sequence, head block, tile) items.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "hdp_internal.h"
+
+namespace hdp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+// Max / sum of a value over lanes l and l^32 (the two half-waves), result in every lane.
+__device__ inline float xhalf_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xhalf_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline int wave_sum(int x) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ inline int wave_max(int x) {
+    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+    return x;
+}
+// Two floats to two bf16 (round to nearest even) in one dword, first in the low half.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Sequence i clamped to [0, Tc]: start and length.  Malformed cu_seqlens give empty sequences.
+__device__ inline void seq_span(const int32_t* cu, int i, int Tc, int& a, int& len) {
+    int s0 = min(max(cu[i], 0), Tc);
+    int s1 = min(max(cu[i + 1], s0), Tc);
+    a = s0;
+    len = s1 - s0;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Longest-first queue.  Sequence i contributes ntiles_i = ceil(len_i / W) tiles for each of the
+// queue's head blocks; a tile's cost level c runs from 1 to ntiles_i (the caller maps c to a
+// tile so that cost grows with c).  Items are handed out level by level from the top, which is
+// longest-processing-time-first order; within a level any order is equivalent.  Everything is
+// derived from cu_seqlens on the device by one wave.
+// ---------------------------------------------------------------------------------------------
+struct QueuePlan {
+    int total;   // items in this queue
+    int maxc;    // highest level
+    int Tc;      // clamped token count
+};
+
+// sum_i max(0, ntiles_i - c)
+__device__ inline int levels_above(const int32_t* cu, int n_seq, int Tc, int W, int c, int lane) {
+    int acc = 0;
+    for (int i = lane; i < n_seq; i += 64) {
+        int a, len;
+        seq_span(cu, i, Tc, a, len);
+        acc += max(0, (len + W - 1) / W - c);
+    }
+    return wave_sum(acc);
+}
+
+// Tbound caps the token count (the caller's row count when it is known).
+__device__ inline QueuePlan queue_plan(const int32_t* cu, int n_seq, int W, int nhbq, int lane,
+                                       int Tbound = 0x7fffffff) {
+    QueuePlan p;
+    p.Tc = min(max(cu[n_seq], 0), Tbound);
+    int sum = 0, mx = 0;
+    for (int i = lane; i < n_seq; i += 64) {
+        int a, len;
+        seq_span(cu, i, p.Tc, a, len);
+        const int nt = (len + W - 1) / W;
+        sum += nt;
+        mx = max(mx, nt);
+    }
+    p.total = wave_sum(sum) * nhbq;
+    p.maxc = wave_max(mx);
+    return p;
+}
+
+// Item k (< total) of the queue -> sequence (a, len), head block index within the queue, level.
+// Returns false only if the plan does not match cu_seqlens (never for k < total).
+__device__ inline bool queue_decode(const int32_t* cu, int n_seq, const QueuePlan& p, int W, int nhbq,
+                                    int k, int lane, int& a, int& len, int& hbq, int& c) {
+    int lo = 1, hi = p.maxc;   // smallest level with levels_above(level) * nhbq <= k
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (levels_above(cu, n_seq, p.Tc, W, mid, lane) * nhbq <= k) hi = mid;
+        else lo = mid + 1;
+    }
+    c = lo;
+    const int j = k - levels_above(cu, n_seq, p.Tc, W, c, lane) * nhbq;
+    int r = j / nhbq;
+    hbq = j % nhbq;
+    int seq = -1;
+    for (int i0 = 0; i0 < n_seq && seq < 0; i0 += 64) {
+        const int i = i0 + lane;
+        bool ok = false;
+        if (i < n_seq) {
+            int sa, sl;
+            seq_span(cu, i, p.Tc, sa, sl);
+            ok = (sl + W - 1) / W >= c;
+        }
+        const uint64_t m = __ballot(ok);
+        const int cnt = __popcll(m);
+        if (r < cnt) {
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            const uint64_t hit = __ballot(ok && below == r);
+            seq = i0 + (int)__builtin_ctzll(hit);
+        } else {
+            r -= cnt;
+        }
+    }
+    if (seq < 0) return false;
+    seq_span(cu, seq, p.Tc, a, len);
+    return true;
+}
+
+// Called by thread 0 of every workgroup after its last pop: the last one out resets the
+// counters, so they are zero again for the next launch on the stream.
+__device__ inline void queue_finish(int* counters) {
+    __threadfence();
+    int* done = &counters[kMaxQueues * kQueueStride];
+    if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
+        for (int qi = 0; qi < kMaxQueues; ++qi) atomicExch(&counters[qi * kQueueStride], 0);
+        atomicExch(done, 0);
+        __threadfence();
+    }
+}
+
+}  // namespace hdp

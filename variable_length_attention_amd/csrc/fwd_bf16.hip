@@ -39,21 +39,10 @@
 // queue per XCD and head block b is served only by the XCD b mod 8, so each K/V head's tiles
 // stay in one XCD's L2.  The order is decoded on the device from cu_seqlens, without a
 // planning launch.
-#include <type_traits>
-
-#include "hdp_internal.h"
+#include "device_common.h"
 
 namespace hdp {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -64,7 +53,6 @@ constexpr int kUnit = 32;             // keys per pipeline step
 constexpr int kStage = 64;            // keys per LDS stage
 constexpr int kStages = 3;            // LDS ring depth
 constexpr float kLazy = 8.0f;         // rescale threshold, log2 units
-constexpr float kLn2 = 0.693147180559945309f;
 
 template <int D>
 struct Cfg {
@@ -76,47 +64,6 @@ struct Cfg {
     static constexpr int kKS = D / 16;                            // k-steps, score product
     static constexpr int kMT = D / 32;                            // D tiles, value product
 };
-
-__device__ inline float xhalf_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float xhalf_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ inline int wave_sum(int x) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
-__device__ inline int wave_max(int x) {
-    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
-// Sequence i clamped to [0, Tc]: start and length.
-__device__ inline void seq_span(const int32_t* cu, int i, int Tc, int& a, int& len) {
-    int s0 = min(max(cu[i], 0), Tc);
-    int s1 = min(max(cu[i + 1], s0), Tc);
-    a = s0;
-    len = s1 - s0;
-}
-
-// Sum over sequences of max(0, ceil(len/W) - c), evaluated by one wave.
-__device__ int levels_above(const int32_t* cu, int n_seq, int Tc, int W, int c, int lane) {
-    int acc = 0;
-    for (int i = lane; i < n_seq; i += 64) {
-        int a, len;
-        seq_span(cu, i, Tc, a, len);
-        int nq = (len + W - 1) / W;
-        acc += max(0, nq - c);
-    }
-    return wave_sum(acc);
-}
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
@@ -142,24 +89,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     const int64_t kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
 
-    // ---- per-launch totals (wave 0 only) ----
-    int total = 0, maxc = 0, Tc = 0;
+    // ---- per-launch queue plan (wave 0 only) ----
+    QueuePlan plan{0, 0, 0};
     if (wave == 0) {
-        if (MODE == 0) {
-            Tc = max(args.cu[args.n_seq], 0);
-            int sum = 0, mx = 0;
-            for (int i = lane; i < args.n_seq; i += 64) {
-                int a, len;
-                seq_span(args.cu, i, Tc, a, len);
-                int nq = (len + W - 1) / W;
-                sum += nq;
-                mx = max(mx, nq);
-            }
-            total = wave_sum(sum) * nhbq;
-            maxc = wave_max(mx);
-        } else {
-            total = ((args.Lq + W - 1) / W) * nhbq;
-        }
+        if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane);
+        else plan.total = ((args.Lq + W - 1) / W) * nhbq;
     }
 
     // per-lane constants of the fragment reads
@@ -174,57 +108,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             int k = 0;
             if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
             k = __shfl(k, 0);
-            if (k >= total) {
-                if (lane == 0) s_item[0] = -1;
-            } else if (MODE == 0) {
-                int lo = 1, hi = maxc;   // smallest level c with levels_above(c) * nhbq <= k
-                while (lo < hi) {
-                    int mid = (lo + hi) >> 1;
-                    if (levels_above(args.cu, args.n_seq, Tc, W, mid, lane) * nhbq <= k) hi = mid;
-                    else lo = mid + 1;
+            int a = 0, len = 0, hbq = 0, c = 0;
+            bool ok = k < plan.total;
+            if (ok) {
+                if (MODE == 0) {
+                    ok = queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
+                } else {
+                    a = 0;
+                    len = args.Lq;
+                    hbq = k % nhbq;
+                    c = ((args.Lq + W - 1) / W) - k / nhbq;
                 }
-                const int c = lo;
-                const int j = k - levels_above(args.cu, args.n_seq, Tc, W, c, lane) * nhbq;
-                int r = j / nhbq;
-                const int hbq = j % nhbq;
-                int seq = -1;
-                for (int i0 = 0; i0 < args.n_seq && seq < 0; i0 += 64) {
-                    int i = i0 + lane;
-                    bool ok = false;
-                    if (i < args.n_seq) {
-                        int a, len;
-                        seq_span(args.cu, i, Tc, a, len);
-                        ok = (len + W - 1) / W >= c;
-                    }
-                    uint64_t m = __ballot(ok);
-                    int cnt = __popcll(m);
-                    if (r < cnt) {
-                        int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-                        uint64_t hit = __ballot(ok && below == r);
-                        seq = i0 + (int)__builtin_ctzll(hit);
-                    } else {
-                        r -= cnt;
-                    }
-                }
-                if (seq < 0) {                 // cannot happen for k < total; stop safely
-                    if (lane == 0) s_item[0] = -1;
-                } else if (lane == 0) {
-                    int a, len;
-                    seq_span(args.cu, seq, Tc, a, len);
-                    s_item[0] = a;
-                    s_item[1] = len;
-                    s_item[2] = queue + nq_queues * hbq;
-                    s_item[3] = c - 1;
-                }
-            } else {
-                if (lane == 0) {
-                    const int nq = (args.Lq + W - 1) / W;
-                    s_item[0] = 0;
-                    s_item[1] = args.Lq;
-                    s_item[2] = queue + nq_queues * (k % nhbq);
-                    s_item[3] = nq - 1 - k / nhbq;
-                }
+            }
+            if (lane == 0) {
+                s_item[0] = ok ? a : -1;
+                s_item[1] = len;
+                s_item[2] = queue + nq_queues * hbq;
+                s_item[3] = c - 1;                 // query tile group: cost grows with it
             }
         }
         __syncthreads();
@@ -512,16 +412,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         __syncthreads();
     }
 
-    // ---- the last workgroup out resets the queue counters for the next launch ----
-    if (tid == 0) {
-        __threadfence();
-        int* done = &args.counters[kMaxQueues * kQueueStride];
-        if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
-            for (int qi = 0; qi < kMaxQueues; ++qi) atomicExch(&args.counters[qi * kQueueStride], 0);
-            atomicExch(done, 0);
-            __threadfence();
-        }
-    }
+    if (tid == 0) queue_finish(args.counters);
 }
 
 }  // namespace

@@ -55,25 +55,26 @@ struct MergeArgs {
 };
 
 struct BwdArgs {
-    const uint16_t* q;
-    const uint16_t* k;
+    const uint16_t* q;      // [T][H][D] bf16
+    const uint16_t* k;      // [T][Hkv][D]
     const uint16_t* v;
-    const uint16_t* out;
-    const float* lse;
-    const uint16_t* dout;
+    const uint16_t* out;    // forward output [T][H][D]
+    const float* lse;       // forward lse [T][H]
+    const uint16_t* dout;   // [T][H][D]
     const int32_t* cu;
     int32_t n_seq;
+    int32_t T;              // caller's row count: every sequence is clamped to it
     int32_t H, Hkv;
     float scale;
     float scale_log2;
-    float* delta;           // [T][H] workspace
-    float* dq_acc;          // [T][H][D] fp32 workspace
+    float* delta;           // [T][H] workspace: rowsum(dO * out), written by the dQ kernel
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
     int* counters;
-    int32_t hpw;
-    int32_t nqueues;
+    int32_t hpw;            // query heads per dQ item
+    int32_t nqueues_q;      // queues of the dQ kernel (8 or 1)
+    int32_t nqueues_kv;     // queues of the dK/dV kernel (8 or 1)
 };
 
 // Launchers (return hipSuccess or the launch error).  `grid` is the persistent grid size.
@@ -81,8 +82,6 @@ hipError_t launch_fwd_varlen(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_chunk(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int D, int grid, int64_t T_upper, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int D, int grid, hipStream_t s);
 
-// Upper bound on the rows a varlen call can touch, unknown on the host; the backward's
-// preprocess walks sequences on the device instead.
 }  // namespace hdp
