@@ -73,22 +73,22 @@ def timed_launches(fn, steps: int, warmup: int, torch):
 
 
 def cpu_baseline(w, q, k, v, cu):
-    """The fp64 oracle on every 2nd row of the slice (all heads), scaled to TFLOP/s."""
-    import numpy as np
-
+    """The fp64 oracle on the whole slice (every row, all heads), repeated until about 10 s of
+    wall time (at most 20 passes), scaled to TFLOP/s."""
     import oracle
 
-    rows = np.arange(0, int(cu[-1]), 2, dtype=np.int64)
-    seq = np.searchsorted(cu, rows, side="right") - 1
-    pairs = int(np.sum(rows - cu[seq] + 1))
-    flops = pairs * w.H * 4 * w.D
-    t0 = time.perf_counter()
-    oracle.varlen_fwd(q, k, v, cu, w.scale, rows=rows)
-    dt = time.perf_counter() - t0
+    flops = sum(int(s) * (int(s) + 1) // 2 for s in w.lengths) * w.H * 4 * w.D
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < 10.0 and len(times) < 20):
+        t0 = time.perf_counter()
+        oracle.varlen_fwd(q, k, v, cu, w.scale)
+        times.append(time.perf_counter() - t0)
+    dt = sum(times) / len(times)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": "every 2nd query row of the same 8192-token slice, all 32 heads "
-                      "(%d rows, %.3g FLOP, %.1f s)" % (len(rows), flops, dt)}
+            "sample": "the whole 8192-token slice (all rows, all 32 heads, %.3g FLOP), %d passes, "
+                      "mean %.2f s per pass" % (flops, len(times), dt)}
 
 
 def detail_rows(torch, ops, synth, steps: int, warmup: int):
@@ -121,6 +121,24 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
                                "merge_us": merge_ms * 1e3,
                                "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9}
     del q, k, v, chunks, acc_o, acc_l, po, pl
+    # backward (and forward + backward) on the 8K slice and on one 8K sequence
+    for make in (synth.fwd_bwd_8k_slice, synth.fwd_bwd_8k_single):
+        w = make()
+        qq, kk, vv, dd = (t.cuda() for t in synth.varlen_tensors(w, with_dout=True))
+        cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
+        o, lse = ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale)
+        dq, dk, dv = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+        _, fwd_ms = timed_launches(lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse),
+                                   steps // 4, warmup, torch)
+        _, bwd_ms = timed_launches(lambda: ops.hdp_attn_varlen_bwd(qq, kk, vv, o, lse, dd, cu, w.scale,
+                                                                   dq=dq, dk=dk, dv=dv), steps // 4, warmup, torch)
+        ff = sum(ops.hdp_seq_flops(s, w.H, w.D, True, 0) for s in w.lengths)
+        fb = sum(ops.hdp_seq_flops(s, w.H, w.D, True, 1) for s in w.lengths)
+        out[w.name] = {"fwd_us": fwd_ms * 1e3, "bwd_us": bwd_ms * 1e3,
+                       "fwd_TFLOP/s": ff / (fwd_ms * 1e-3) / 1e12,
+                       "bwd_TFLOP/s": fb / (bwd_ms * 1e-3) / 1e12,
+                       "fwd_bwd_TFLOP/s": (ff + fb) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12}
+        del qq, kk, vv, dd, o, lse, dq, dk, dv
     for make in (synth.microbatch_32k_long, synth.microbatch_32k_short):
         w = make()
         qq, kk, vv = (t.cuda() for t in synth.varlen_tensors(w))
@@ -142,6 +160,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy 512 MiB device-to-device 3 times (a known-size kernel that "
+                         "calibrates the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the per-rank kernel "
@@ -154,6 +175,14 @@ def main() -> int:
     from variable_length_attention_amd import ops, synth
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = synth.packed_slice_8k()
     q, k, v = synth.varlen_tensors(w)
     cu = synth.cu_seqlens(w.lengths)
