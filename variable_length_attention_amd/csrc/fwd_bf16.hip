@@ -355,9 +355,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; l[nt] = 0.f; }
 
-        auto softmax_lazy = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2]) {
-            float tmax[kNT];
+        // Softmax of one unit against the current running max (no branch).  P can exceed 2^8
+        // only when a row max grew; fix_rescale then raises the max, rescales what was
+        // accumulated before this unit and recomputes this unit's P and sum (rare, branch).
+        auto softmax_deferred = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2], float (&tmax)[kNT],
+                                    float (&lb)[kNT]) {
             row_max(S, tmax);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) lb[nt] = l[nt];
+            exponentials(S, m, l, P);
+        };
+        auto fix_rescale = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2], const float (&tmax)[kNT],
+                               const float (&lb)[kNT]) {
             bool need = false;
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) need |= tmax[nt] > m[nt] + kLazy;
@@ -367,36 +376,94 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     const float mn = fmaxf(m[nt], tmax[nt]);
                     const float alpha = (m[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mn);
                     m[nt] = mn;
-                    l[nt] *= alpha;
+                    l[nt] = lb[nt] * alpha;
 #pragma unroll
                     for (int mt = 0; mt < C::kMT; ++mt) o[mt][nt] *= alpha;
                 }
+                exponentials(S, m, l, P);
             }
-            exponentials(S, m, l, P);
         };
 
+        // Every step has the same shape: step u runs the value product of unit u-1 (P of unit -1
+        // is zero), the score product of unit u+1 (discarded after the last unit) and the
+        // softmax of unit u, as one straight-line block whose MFMAs the scheduling barriers
+        // interleave with the softmax VALU work.  The rare branches come after it: the rescale
+        // of unit u, and the mask of unit u+1 (masked units only reach past the diagonal or
+        // the last key, i.e. at the end of an item).
         if (n_units > 0) {
             f32x16 Sc[kNT], Sn[kNT];
             bf16x8 Pp[kNT][2], Pc[kNT][2];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                Pp[nt][0] = bf16x8{};
+                Pp[nt][1] = bf16x8{};
+            }
             {
                 u32x4 kf[C::kKS];
                 read_k(0, kf);
                 score(kf, Sc);
             }
+            if (!unit_full(0)) apply_mask(0, Sc);
             for (int u = 0; u < n_units; ++u) {
                 stage_turn(u);
-                if (u >= 1) {
-                    bf16x8 vf[2][C::kMT];
-                    read_v(u - 1, vf);
-                    value(o, vf, Pp);
+                bf16x8 vf[2][C::kMT];
+                u32x4 kf[C::kKS];
+                read_v(max(u - 1, 0), vf);
+                read_k(u + 1, kf);
+                __builtin_amdgcn_sched_barrier(0);
+                // 32 slots: one MFMA (16 value-product, then 16 score-product MFMAs) and the
+                // softmax work of one score element (against the current max: no dependency
+                // on this unit's max), in this order; sched_barrier keeps the order.
+                constexpr int kPV = 2 * C::kMT * kNT;
+                constexpr int kQK = C::kKS * kNT;
+                constexpr int kElems = 16 * kNT;                       // score elements per lane
+                constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
+                float mb[kNT], mx[kNT], ls[kNT], lb[kNT];
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    mb[nt] = (m[nt] == -INFINITY) ? 0.f : m[nt];
+                    mx[nt] = -INFINITY;
+                    ls[nt] = 0.f;
+                    lb[nt] = l[nt];
+                    Sn[nt] = f32x16{};
                 }
-                if (u + 1 < n_units) {
-                    u32x4 kf[C::kKS];
-                    read_k(u + 1, kf);
-                    score(kf, Sn);
+#pragma unroll
+                for (int k = 0; k < kSlots; ++k) {
+                    if (k >= kPV + kQK) {
+                        // (D = 64: more score elements than MFMAs)
+                    } else if (k < kPV) {
+                        const int ks2 = k / (C::kMT * kNT), mt = (k / kNT) % C::kMT, nt = k % kNT;
+                        o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks2][mt], Pp[nt][ks2], o[mt][nt], 0, 0, 0);
+                    } else {
+                        const int ks = (k - kPV) / kNT, nt = (k - kPV) % kNT;
+                        Sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[nt][ks]), Sn[nt], 0, 0, 0);
+                    }
+                    // score element e = k of this unit
+                    if (k < kElems) {
+                        const int nt = k / 16, i = k % 16;
+                        const float sv = Sc[nt][i];
+                        mx[nt] = fmaxf(mx[nt], sv);
+                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -mb[nt]));
+                        ls[nt] += pv;
+                        Pc[nt][i >> 3][i & 7] = (__bf16)pv;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                if (!unit_full(u)) apply_mask(u, Sc);
-                softmax_lazy(Sc, Pc);
+                float tmax[kNT];
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    tmax[nt] = xhalf_max(mx[nt]) * c2;
+                    l[nt] += ls[nt];
+                }
+                // Pin this step's softmax results here, so the compiler cannot sink them into
+                // the no-rescale side of the rare branch below.
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    asm volatile("" : "+v"(Pc[nt][0]), "+v"(Pc[nt][1]), "+v"(l[nt]));
+                }
+                fix_rescale(Sc, Pc, tmax, lb);
+                if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
                     Sc[nt] = Sn[nt];
