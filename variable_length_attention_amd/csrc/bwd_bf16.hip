@@ -41,14 +41,14 @@ struct Cfg {
     static constexpr int kMT = D / 32;
 };
 
-// ---- LDS tile helpers: rows of D bf16, 16-byte slots XOR-swizzled by (row & 7) ----
+// ---- LDS tile helpers: rows of D bf16, 16-byte slots XOR-swizzled by swz(row) ----
 
 // A-operand fragment rows (row = tile row of this lane): 8 bf16 of d = ks*16 + half*8.
 template <int D>
 __device__ inline void lds_rows_frag(const unsigned char* tile, int row, int half, u32x4 (&f)[Cfg<D>::kKS]) {
 #pragma unroll
     for (int ks = 0; ks < Cfg<D>::kKS; ++ks) {
-        const int slot = (2 * ks + half) ^ (row & 7);
+        const int slot = (2 * ks + half) ^ swz(row);
         f[ks] = *(const u32x4*)(tile + row * Cfg<D>::kRowBytes + slot * 16);
     }
 }
@@ -69,8 +69,8 @@ __device__ inline void lds_cols_frag(const unsigned char* tile, int r_base, int 
             const int chunk = (mt * 32 + tr_col) >> 3;
             const int r0 = r_base + 16 * ks2 + tr_row;
             const int r1 = r0 + 8;
-            const unsigned char* p0 = tile + r0 * Cfg<D>::kRowBytes + ((chunk ^ (r0 & 7)) << 4) + tr_sub;
-            const unsigned char* p1 = tile + r1 * Cfg<D>::kRowBytes + ((chunk ^ (r1 & 7)) << 4) + tr_sub;
+            const unsigned char* p0 = tile + r0 * Cfg<D>::kRowBytes + ((chunk ^ swz(r0)) << 4) + tr_sub;
+            const unsigned char* p1 = tile + r1 * Cfg<D>::kRowBytes + ((chunk ^ swz(r1)) << 4) + tr_sub;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
             f[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
@@ -85,7 +85,7 @@ __device__ inline void dma_block(const uint16_t* src, int64_t stride, int64_t ba
                                  int blk, int lane, unsigned char* tile) {
     const int row = blk * Cfg<D>::kRowsPerBlock + lane / Cfg<D>::kChunks;
     const int slot = lane % Cfg<D>::kChunks;
-    const int chunk = slot ^ (row & 7);
+    const int chunk = slot ^ swz(row);
     const int64_t r = base_row + min(row, last_row);
     __builtin_amdgcn_global_load_lds(src + r * stride + chunk * 8, (lds_void*)(tile + blk * 1024), 16, 0, 0);
 }

@@ -47,6 +47,12 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// LDS slot swizzle of a row: the 16-byte slot holding chunk c of row r is c ^ swz(r).  swz maps
+// any 8 consecutive rows to 8 different values (score-operand reads: 32 rows, one chunk) and
+// any 4 rows 4k..4k+3 to values whose pairwise XOR is neither 0 nor 1 (transposing reads: 4
+// rows x 2 adjacent chunks), so neither read kind hits a bank twice in one LDS cycle.
+__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
 // Sequence i clamped to [0, Tc]: start and length.  Malformed cu_seqlens give empty sequences.
 __device__ inline void seq_span(const int32_t* cu, int i, int Tc, int& a, int& len) {
     int s0 = min(max(cu[i], 0), Tc);

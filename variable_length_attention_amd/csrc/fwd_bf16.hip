@@ -25,7 +25,7 @@
 // the vector ALUs; the three are independent.  K/V arrive in stages of 64 keys through direct
 // global->LDS loads (global_load_lds_dwordx4, no registers), three stages deep, one workgroup
 // barrier per stage.  LDS rows are unpadded and their 16-byte slots are XOR-swizzled by the
-// row index, so the rows a fragment read touches fall on different banks.
+// row index (swz), so neither fragment read kind hits a bank twice in one cycle.
 //
 // Softmax uses exp2 with scale*log2(e) folded into one FMA, and a lazy running max: the
 // accumulator is rescaled only when some row's max grows by more than 2^8, which keeps every
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 const int blk = wave * C::kBlocksPerWave + i;
                 const int row = blk * C::kRowsPerBlock + lane / C::kChunks;
                 const int slot = lane % C::kChunks;
-                const int chunk = slot ^ (row & 7);
+                const int chunk = slot ^ swz(row);
                 const int j = min(st * kStage + row, sk - 1);    // clamp into this sequence
                 const int64_t off = (kbase + j) * kv_stride + (int64_t)g * D + chunk * 8;
                 __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             const int row = (u & 1) * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks) {
-                const int slot = (2 * ks + half) ^ (row & 7);
+                const int slot = (2 * ks + half) ^ swz(row);
                 kf[ks] = *(const u32x4*)(kb + row * C::kRowBytes + slot * 16);
             }
         };
@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     const int chunk = (mt * 32 + tr_col) >> 3;
                     const int r0 = (u & 1) * 32 + 16 * ks2 + tr_row;
                     const int r1 = r0 + 8;
-                    const unsigned char* p0 = vb + r0 * C::kRowBytes + ((chunk ^ (r0 & 7)) << 4) + tr_sub;
-                    const unsigned char* p1 = vb + r1 * C::kRowBytes + ((chunk ^ (r1 & 7)) << 4) + tr_sub;
+                    const unsigned char* p0 = vb + r0 * C::kRowBytes + ((chunk ^ swz(r0)) << 4) + tr_sub;
+                    const unsigned char* p1 = vb + r1 * C::kRowBytes + ((chunk ^ swz(r1)) << 4) + tr_sub;
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
                     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
                     vf[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
@@ -280,15 +280,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 ll[nt] += ls;
             }
         };
-        // stage ring: at odd u, stage (u+3)/2 goes into the buffer of stage (u-3)/2 (last read
+        // stage ring (called at odd u only): stage (u+3)/2 goes into the buffer of stage (u-3)/2 (last read
         // in iteration u-1 or earlier); stage (u+1)/2, issued at u-2, must have landed.
         auto stage_turn = [&](int u) {
-            if (u & 1) {
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-                __syncthreads();
-                const int st = (u + 3) >> 1;
-                if (st < n_stages) load_stage(st);
-            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            __syncthreads();
+            const int st = (u + 3) >> 1;
+            if (st < n_stages) load_stage(st);
         };
         auto stage_prologue = [&]() {
             if (n_units > 0) {
@@ -389,91 +387,100 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // softmax of unit u, as one straight-line block whose MFMAs the scheduling barriers
         // interleave with the softmax VALU work.  The rare branches come after it: the rescale
         // of unit u, and the mask of unit u+1 (masked units only reach past the diagonal or
-        // the last key, i.e. at the end of an item).
-        if (n_units > 0) {
-            f32x16 Sc[kNT], Sn[kNT];
-            bf16x8 Pp[kNT][2], Pc[kNT][2];
+        // the last key, i.e. at the end of an item).  Steps go in pairs that swap the roles of
+        // two score and two probability buffers, so no registers are copied between steps.
+        auto step = [&](int u, bool odd, f32x16 (&Sc)[kNT], f32x16 (&Sn)[kNT], const bf16x8 (&Pp)[kNT][2],
+                        bf16x8 (&Pc)[kNT][2]) {
+            if (odd) stage_turn(u);
+            bf16x8 vf[2][C::kMT];
+            u32x4 kf[C::kKS];
+            read_v(max(u - 1, 0), vf);
+            read_k(u + 1, kf);
+            __builtin_amdgcn_sched_barrier(0);
+            // 32 slots: one MFMA (16 value-product, then 16 score-product MFMAs) and the
+            // softmax work of one score element (against the current max: no dependency on
+            // this unit's max), in this order; sched_barrier keeps the order.
+            constexpr int kPV = 2 * C::kMT * kNT;
+            constexpr int kQK = C::kKS * kNT;
+            constexpr int kElems = 16 * kNT;                       // score elements per lane
+            constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
+            float mb[kNT], mx[kNT], ls[kNT], lb[kNT];
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                Pp[nt][0] = bf16x8{};
-                Pp[nt][1] = bf16x8{};
+                mb[nt] = (m[nt] == -INFINITY) ? 0.f : m[nt];
+                mx[nt] = -INFINITY;
+                ls[nt] = 0.f;
+                lb[nt] = l[nt];
+                Sn[nt] = f32x16{};
+            }
+#pragma unroll
+            for (int k = 0; k < kSlots; ++k) {
+                if (k >= kPV + kQK) {
+                    // (D = 64: more score elements than MFMAs)
+                } else if (k < kPV) {
+                    const int ks2 = k / (C::kMT * kNT), mt = (k / kNT) % C::kMT, nt = k % kNT;
+                    o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks2][mt], Pp[nt][ks2], o[mt][nt], 0, 0, 0);
+                } else {
+                    const int ks = (k - kPV) / kNT, nt = (k - kPV) % kNT;
+                    Sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[nt][ks]), Sn[nt], 0, 0, 0);
+                }
+                // score element e = k of this unit
+                if (k < kElems) {
+                    const int nt = k / 16, i = k % 16;
+                    const float sv = Sc[nt][i];
+                    mx[nt] = fmaxf(mx[nt], sv);
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -mb[nt]));
+                    ls[nt] += pv;
+                    Pc[nt][i >> 3][i & 7] = (__bf16)pv;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float tmax[kNT];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                tmax[nt] = xhalf_max(mx[nt]) * c2;
+                l[nt] += ls[nt];
+            }
+            // Pin this step's softmax results here, so the compiler cannot sink them into the
+            // no-rescale side of the rare branch below.
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                asm volatile("" : "+v"(Pc[nt][0]), "+v"(Pc[nt][1]), "+v"(l[nt]));
+            }
+            fix_rescale(Sc, Pc, tmax, lb);
+            if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
+        };
+        auto finish = [&](const bf16x8 (&P)[kNT][2]) {
+            bf16x8 vf[2][C::kMT];
+            read_v(n_units - 1, vf);
+            value(o, vf, P);
+        };
+        if (n_units > 0) {
+            f32x16 SA[kNT], SB[kNT];
+            bf16x8 PA[kNT][2], PB[kNT][2];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                PA[nt][0] = bf16x8{};
+                PA[nt][1] = bf16x8{};
             }
             {
                 u32x4 kf[C::kKS];
                 read_k(0, kf);
-                score(kf, Sc);
+                score(kf, SA);
             }
-            if (!unit_full(0)) apply_mask(0, Sc);
-            for (int u = 0; u < n_units; ++u) {
-                stage_turn(u);
-                bf16x8 vf[2][C::kMT];
-                u32x4 kf[C::kKS];
-                read_v(max(u - 1, 0), vf);
-                read_k(u + 1, kf);
-                __builtin_amdgcn_sched_barrier(0);
-                // 32 slots: one MFMA (16 value-product, then 16 score-product MFMAs) and the
-                // softmax work of one score element (against the current max: no dependency
-                // on this unit's max), in this order; sched_barrier keeps the order.
-                constexpr int kPV = 2 * C::kMT * kNT;
-                constexpr int kQK = C::kKS * kNT;
-                constexpr int kElems = 16 * kNT;                       // score elements per lane
-                constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
-                float mb[kNT], mx[kNT], ls[kNT], lb[kNT];
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    mb[nt] = (m[nt] == -INFINITY) ? 0.f : m[nt];
-                    mx[nt] = -INFINITY;
-                    ls[nt] = 0.f;
-                    lb[nt] = l[nt];
-                    Sn[nt] = f32x16{};
-                }
-#pragma unroll
-                for (int k = 0; k < kSlots; ++k) {
-                    if (k >= kPV + kQK) {
-                        // (D = 64: more score elements than MFMAs)
-                    } else if (k < kPV) {
-                        const int ks2 = k / (C::kMT * kNT), mt = (k / kNT) % C::kMT, nt = k % kNT;
-                        o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks2][mt], Pp[nt][ks2], o[mt][nt], 0, 0, 0);
-                    } else {
-                        const int ks = (k - kPV) / kNT, nt = (k - kPV) % kNT;
-                        Sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[nt][ks]), Sn[nt], 0, 0, 0);
-                    }
-                    // score element e = k of this unit
-                    if (k < kElems) {
-                        const int nt = k / 16, i = k % 16;
-                        const float sv = Sc[nt][i];
-                        mx[nt] = fmaxf(mx[nt], sv);
-                        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -mb[nt]));
-                        ls[nt] += pv;
-                        Pc[nt][i >> 3][i & 7] = (__bf16)pv;
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                float tmax[kNT];
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    tmax[nt] = xhalf_max(mx[nt]) * c2;
-                    l[nt] += ls[nt];
-                }
-                // Pin this step's softmax results here, so the compiler cannot sink them into
-                // the no-rescale side of the rare branch below.
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    asm volatile("" : "+v"(Pc[nt][0]), "+v"(Pc[nt][1]), "+v"(l[nt]));
-                }
-                fix_rescale(Sc, Pc, tmax, lb);
-                if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    Sc[nt] = Sn[nt];
-                    Pp[nt][0] = Pc[nt][0];
-                    Pp[nt][1] = Pc[nt][1];
-                }
+            if (!unit_full(0)) apply_mask(0, SA);
+            int u = 0;
+            for (; u + 1 < n_units; u += 2) {
+                step(u, false, SA, SB, PA, PB);
+                step(u + 1, true, SB, SA, PB, PA);
             }
-            bf16x8 vf[2][C::kMT];
-            read_v(n_units - 1, vf);
-            value(o, vf, Pp);
+            if (u < n_units) {
+                step(u, false, SA, SB, PA, PB);
+                finish(PB);
+            } else {
+                finish(PA);
+            }
         }
         store_rows(o, m, l);
         __syncthreads();
