@@ -27,10 +27,12 @@
 // barrier per stage.  LDS rows are unpadded and their 16-byte slots are XOR-swizzled by the
 // row index (swz), so neither fragment read kind hits a bank twice in one cycle.
 //
-// Softmax uses exp2 with scale*log2(e) folded into one FMA, and a lazy running max: the
-// accumulator is rescaled only when some row's max grows by more than 2^8, which keeps every
-// P <= 256 (exact arithmetic is unchanged because the same reference max is used for the
-// numerator and the denominator).
+// Softmax uses exp2 with scale*log2(e) folded into one FMA and a lazy reference instead of an
+// exact running max (exact arithmetic is unchanged because numerator and denominator share the
+// reference).  The common path computes no max at all: P = exp2(S c2 - m) is summed in fp32
+// and goes straight to bf16.  Only when a lane's sum over a unit exceeds 2^8 (so possibly
+// some P > 2^8), or on a row's first visible unit, does a branch take the row max, raise the
+// reference and rescale the accumulator.
 //
 // Scheduling.  The kernel is persistent (one workgroup per CU).  Items are popped from a queue
 // in order of decreasing cost, where the cost of a query tile is the number of key tiles it
@@ -52,7 +54,7 @@ constexpr int kItemRowHeads = 256;    // query (row, head) pairs per item
 constexpr int kUnit = 32;             // keys per pipeline step
 constexpr int kStage = 64;            // keys per LDS stage
 constexpr int kStages = 3;            // LDS ring depth
-constexpr float kLazy = 8.0f;         // rescale threshold, log2 units
+constexpr float kLazySum = 256.0f;    // rescale when a lane's unit sum of P exceeds 2^8
 
 template <int D>
 struct Cfg {
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             const int j0 = u * kUnit;
             return (j0 + kUnit - 1 < sk) && (!causal || j0 + kUnit - 1 <= delta + r_lo);
         };
-        // row max of a unit in log2 units (both half-waves)
+        // row max of a unit in log2 units (both half-waves); rescale branch only
         auto row_max = [&](const f32x16 (&S)[kNT], float (&tmax)[kNT]) {
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 tmax[nt] = xhalf_max(mx) * c2;
             }
         };
-        // P^T = exp2(S c2 - m) as bf16 B operands, row sums into ll
+        // P^T = exp2(S c2 - m) as bf16 B operands, row sums (fp32, before rounding) into ll
         auto exponentials = [&](const f32x16 (&S)[kNT], const float (&mm)[kNT], float (&ll)[kNT], bf16x8 (&P)[kNT][2]) {
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
@@ -339,42 +341,39 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
 
         // ---- software-pipelined units with a lazily rescaled running max ----
         // Step u issues the value product of unit u-1 and the score product of unit u+1 and
-        // runs the softmax of unit u; the three are independent.  The running max is raised
-        // (and the accumulator rescaled) only when some row's max grows by more than 2^8, which
-        // keeps every P <= 256; numerator and denominator share the reference, so the result is
-        // exact whatever reference is used.
+        // runs the softmax of unit u; the three are independent.  The running max m is a
+        // reference, not necessarily the max: numerator and denominator share it, so the result
+        // is exact whatever reference is used as long as no P overflows or all underflow.  It is
+        // raised (and the accumulator rescaled) only when a lane's sum of P over a unit exceeds
+        // 2^8, which keeps every P <= 2^8, and on a row's first visible unit.
         stage_prologue();
         f32x16 o[C::kMT][kNT];
 #pragma unroll
         for (int mt = 0; mt < C::kMT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) o[mt][nt] = f32x16{};
-        float m[kNT], l[kNT];
+        float m[kNT], l[kNT], thr[kNT];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; l[nt] = 0.f; }
+        for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; l[nt] = 0.f; thr[nt] = -1.f; }
 
-        // Softmax of one unit against the current running max (no branch).  P can exceed 2^8
-        // only when a row max grew; fix_rescale then raises the max, rescales what was
-        // accumulated before this unit and recomputes this unit's P and sum (rare, branch).
-        auto softmax_deferred = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2], float (&tmax)[kNT],
-                                    float (&lb)[kNT]) {
-            row_max(S, tmax);
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) lb[nt] = l[nt];
-            exponentials(S, m, l, P);
-        };
-        auto fix_rescale = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2], const float (&tmax)[kNT],
+        // Runs when some lane's unit sum ls passed its threshold: raises the reference to the
+        // row max (in log2 units), rescales what was accumulated before this unit (its sum lb)
+        // and recomputes this unit's P and sum.  Rare: a branch after the step.
+        auto fix_rescale = [&](f32x16 (&S)[kNT], bf16x8 (&P)[kNT][2], const float (&ls)[kNT],
                                const float (&lb)[kNT]) {
             bool need = false;
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) need |= tmax[nt] > m[nt] + kLazy;
+            for (int nt = 0; nt < kNT; ++nt) need |= ls[nt] > thr[nt];
             if (__ballot(need)) {
+                float tmax[kNT];
+                row_max(S, tmax);
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
                     const float mn = fmaxf(m[nt], tmax[nt]);
                     const float alpha = (m[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mn);
                     m[nt] = mn;
                     l[nt] = lb[nt] * alpha;
+                    thr[nt] = (mn == -INFINITY) ? -1.f : kLazySum;
 #pragma unroll
                     for (int mt = 0; mt < C::kMT; ++mt) o[mt][nt] *= alpha;
                 }
@@ -385,36 +384,41 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // Every step has the same shape: step u runs the value product of unit u-1 (P of unit -1
         // is zero), the score product of unit u+1 (discarded after the last unit) and the
         // softmax of unit u, as one straight-line block whose MFMAs the scheduling barriers
-        // interleave with the softmax VALU work.  The rare branches come after it: the rescale
-        // of unit u, and the mask of unit u+1 (masked units only reach past the diagonal or
-        // the last key, i.e. at the end of an item).  Steps go in pairs that swap the roles of
-        // two score and two probability buffers, so no registers are copied between steps.
+        // interleave with the softmax VALU work.  The V^T fragments of unit u are read from LDS
+        // in the middle of step u, once the value product of unit u-1 has been issued, so they
+        // are in registers when step u+1 starts.  The rare branches come after the block: the
+        // rescale of unit u, and the mask of unit u+1 (masked units only reach past the
+        // diagonal or the last key, i.e. at the end of an item).  Steps go in pairs that swap
+        // the roles of two score and two probability buffers, so no registers are copied
+        // between steps.
+        bf16x8 vf[2][C::kMT];
         auto step = [&](int u, bool odd, f32x16 (&Sc)[kNT], f32x16 (&Sn)[kNT], const bf16x8 (&Pp)[kNT][2],
                         bf16x8 (&Pc)[kNT][2]) {
             if (odd) stage_turn(u);
-            bf16x8 vf[2][C::kMT];
             u32x4 kf[C::kKS];
-            read_v(max(u - 1, 0), vf);
             read_k(u + 1, kf);
             __builtin_amdgcn_sched_barrier(0);
-            // 32 slots: one MFMA (16 value-product, then 16 score-product MFMAs) and the
-            // softmax work of one score element (against the current max: no dependency on
-            // this unit's max), in this order; sched_barrier keeps the order.
+            // 32 slots: one MFMA (value-product MFMAs, then score-product MFMAs) and the softmax
+            // work of one score element (against the current reference: no dependency on this
+            // unit's max), in this order; sched_barrier keeps the order.
             constexpr int kPV = 2 * C::kMT * kNT;
             constexpr int kQK = C::kKS * kNT;
             constexpr int kElems = 16 * kNT;                       // score elements per lane
             constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
-            float mb[kNT], mx[kNT], ls[kNT], lb[kNT];
+            float mb[kNT], ls[kNT], lb[kNT];
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 mb[nt] = (m[nt] == -INFINITY) ? 0.f : m[nt];
-                mx[nt] = -INFINITY;
                 ls[nt] = 0.f;
                 lb[nt] = l[nt];
                 Sn[nt] = f32x16{};
             }
 #pragma unroll
             for (int k = 0; k < kSlots; ++k) {
+                if (k == kPV) {
+                    read_v(u, vf);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (k >= kPV + kQK) {
                     // (D = 64: more score elements than MFMAs)
                 } else if (k < kPV) {
@@ -428,34 +432,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 // score element e = k of this unit
                 if (k < kElems) {
                     const int nt = k / 16, i = k % 16;
-                    const float sv = Sc[nt][i];
-                    mx[nt] = fmaxf(mx[nt], sv);
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -mb[nt]));
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[nt][i], c2, -mb[nt]));
                     ls[nt] += pv;
                     Pc[nt][i >> 3][i & 7] = (__bf16)pv;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            float tmax[kNT];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                tmax[nt] = xhalf_max(mx[nt]) * c2;
-                l[nt] += ls[nt];
-            }
+            for (int nt = 0; nt < kNT; ++nt) l[nt] += ls[nt];
             // Pin this step's softmax results here, so the compiler cannot sink them into the
             // no-rescale side of the rare branch below.
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 asm volatile("" : "+v"(Pc[nt][0]), "+v"(Pc[nt][1]), "+v"(l[nt]));
             }
-            fix_rescale(Sc, Pc, tmax, lb);
+            fix_rescale(Sc, Pc, ls, lb);
             if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
         };
-        auto finish = [&](const bf16x8 (&P)[kNT][2]) {
-            bf16x8 vf[2][C::kMT];
-            read_v(n_units - 1, vf);
-            value(o, vf, P);
-        };
+        auto finish = [&](const bf16x8 (&P)[kNT][2]) { value(o, vf, P); };   // vf holds unit n-1
         if (n_units > 0) {
             f32x16 SA[kNT], SB[kNT];
             bf16x8 PA[kNT][2], PB[kNT][2];
@@ -469,6 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 read_k(0, kf);
                 score(kf, SA);
             }
+            read_v(0, vf);   // multiplied by the zero P of unit -1
             if (!unit_full(0)) apply_mask(0, SA);
             int u = 0;
             for (; u + 1 < n_units; u += 2) {
