@@ -18,6 +18,19 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+// base + off behind an optimisation barrier: the optimiser cannot re-associate the sum with
+// the immediates added later, so those stay instruction offsets of the LDS reads
+__device__ inline uint32_t lds_add(uint32_t base, uint32_t off) {
+    uint32_t r = base + off;
+    asm volatile("" : "+v"(r));
+    return r;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;

@@ -103,6 +103,33 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     const int tr_row = 4 * (gidx >> 1) + ((lane & 15) >> 2);
     const int tr_col = 16 * (gidx & 1) + 4 * (lane & 3);          // bf16 column within 32
     const int tr_sub = (lane & 1) * 8;                            // byte offset within a slot
+    // Byte offsets of this lane's fragment reads within a 32-row unit of a tile.  Rows 8 apart
+    // share the swizzle, so the XOR only mixes the low slot bits: a read's slot is a per-lane
+    // part (XOR of a few compile-time bits) plus a compile-time part, which becomes the
+    // instruction's immediate offset.  K: slot of k-step ks = (2 ks + half) ^ swz(row).
+    int kofs[4];
+    {
+        const int t = half ^ swz(l32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kofs[j] = l32 * C::kRowBytes + 16 * ((2 * j) ^ t);
+    }
+    // Stage loads: element offset of this lane's 16-byte chunk in each of its 1 KB blocks,
+    // relative to the stage's first key row of the head (the LDS slot of a chunk is fixed by
+    // the lane).
+    int gofs[C::kBlocksPerWave];
+#pragma unroll
+    for (int i = 0; i < C::kBlocksPerWave; ++i) {
+        const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
+        const int chunk = (lane % C::kChunks) ^ swz(row);
+        gofs[i] = (int)(row * kv_stride + chunk * 8);
+    }
+    // V^T: slot of D tile mt = (4 mt + c) ^ swz(tr_row), c = column / 8 within the tile
+    int vofs[2];
+    {
+        const int t = (tr_col >> 3) ^ swz(tr_row);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) vofs[j] = tr_row * C::kRowBytes + 16 * ((4 * j) ^ t) + tr_sub;
+    }
 
     for (;;) {
         // ---- pop and decode the next item (wave 0) ----
@@ -173,47 +200,65 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         for (int nt = 0; nt < kNT; ++nt)
             lim0[nt] = causal ? delta + r_lo + nt * 32 + l32 : sk - 1;
 
-        // ---- direct global -> LDS stage loads (K and V of 64 keys) ----
-        auto load_stage = [&](int st) {
-            unsigned char* kb = smem[st % kStages][0];
-            unsigned char* vb = smem[st % kStages][1];
+        // ---- direct global -> LDS stage loads (K and V of 64 keys) into ring buffer B ----
+        // A whole stage inside the sequence takes a scalar base plus the per-lane offsets; the
+        // last stage clamps its rows to the sequence's last key.
+        auto load_stage = [&](int st, int B) {
+            unsigned char* kb = smem[B][0];
+            unsigned char* vb = smem[B][1];
+            const int j0 = st * kStage;
+            if (j0 + kStage <= sk) {
 #pragma unroll
-            for (int i = 0; i < C::kBlocksPerWave; ++i) {
-                const int blk = wave * C::kBlocksPerWave + i;
-                const int row = blk * C::kRowsPerBlock + lane / C::kChunks;
-                const int slot = lane % C::kChunks;
-                const int chunk = slot ^ swz(row);
-                const int j = min(st * kStage + row, sk - 1);    // clamp into this sequence
-                const int64_t off = (kbase + j) * kv_stride + (int64_t)g * D + chunk * 8;
-                __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+                for (int i = 0; i < C::kBlocksPerWave; ++i) {
+                    const int blk = wave * C::kBlocksPerWave + i;
+                    const int64_t off = (kbase + j0) * kv_stride + (int64_t)g * D + gofs[i];
+                    __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::kBlocksPerWave; ++i) {
+                    const int blk = wave * C::kBlocksPerWave + i;
+                    const int row = blk * C::kRowsPerBlock + lane / C::kChunks;
+                    const int chunk = (lane % C::kChunks) ^ swz(row);
+                    const int j = min(j0 + row, sk - 1);
+                    const int64_t off = (kbase + j) * kv_stride + (int64_t)g * D + chunk * 8;
+                    __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
+                    __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+                }
             }
         };
 
-        // K fragments of unit u (A operand of the score product), read from LDS
-        auto read_k = [&](int u, u32x4 (&kf)[C::kKS]) {
-            const unsigned char* kb = smem[(u >> 1) % kStages][0];
-            const int row = (u & 1) * 32 + l32;
-#pragma unroll
-            for (int ks = 0; ks < C::kKS; ++ks) {
-                const int slot = (2 * ks + half) ^ swz(row);
-                kf[ks] = *(const u32x4*)(kb + row * C::kRowBytes + slot * 16);
-            }
+        // LDS base of unit u's rows in the K (kv = 0) or V (kv = 1) ring buffer: uniform
+        auto unit_base = [&](int u, int kv) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(lds_addr(smem[(u >> 1) % kStages][kv]) + (u & 1) * 32 * C::kRowBytes));
         };
-        // V^T fragments of unit u (A operand of the value product), transposing LDS reads
+        // K fragments of unit u (A operand of the score product): 4 lane addresses, the
+        // k-steps differ by immediate offsets
+        auto read_k = [&](int u, u32x4 (&kf)[C::kKS]) {
+            const uint32_t kb = unit_base(u, 0);
+            uint32_t a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = lds_add(kb, kofs[j]);
+#pragma unroll
+            for (int ks = 0; ks < C::kKS; ++ks)
+                kf[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
+        };
+        // V^T fragments of unit u (A operand of the value product), transposing LDS reads: for
+        // k-step ks2 and D tile mt, lane l receives 8 values of column mt*32 + l%32 from the
+        // unit's rows 16 ks2 + 8 (i/4) + 4 (l/32) + i%4 (the accumulator row order)
         auto read_v = [&](int u, bf16x8 (&vf)[2][C::kMT]) {
-            const unsigned char* vb = smem[(u >> 1) % kStages][1];
+            const uint32_t vb = unit_base(u, 1);
+            const uint32_t a[2] = {lds_add(vb, vofs[0]), lds_add(vb, vofs[1])};
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
                 for (int mt = 0; mt < C::kMT; ++mt) {
-                    const int chunk = (mt * 32 + tr_col) >> 3;
-                    const int r0 = (u & 1) * 32 + 16 * ks2 + tr_row;
-                    const int r1 = r0 + 8;
-                    const unsigned char* p0 = vb + r0 * C::kRowBytes + ((chunk ^ swz(r0)) << 4) + tr_sub;
-                    const unsigned char* p1 = vb + r1 * C::kRowBytes + ((chunk ^ swz(r1)) << 4) + tr_sub;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+                    const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
                     vf[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
                     vf[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
                 }
@@ -288,12 +333,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             __syncthreads();
             const int st = (u + 3) >> 1;
-            if (st < n_stages) load_stage(st);
+            if (st < n_stages) load_stage(st, st % kStages);
         };
         auto stage_prologue = [&]() {
             if (n_units > 0) {
-                load_stage(0);
-                if (n_stages > 1) load_stage(1);
+                load_stage(0, 0);
+                if (n_stages > 1) load_stage(1, 1);
                 __builtin_amdgcn_s_waitcnt(0x0F70);
             }
             __syncthreads();
@@ -449,7 +494,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             fix_rescale(Sc, Pc, ls, lb);
             if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
         };
-        auto finish = [&](const bf16x8 (&P)[kNT][2]) { value(o, vf, P); };   // vf holds unit n-1
         if (n_units > 0) {
             f32x16 SA[kNT], SB[kNT];
             bf16x8 PA[kNT][2], PB[kNT][2];
@@ -470,11 +514,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 step(u, false, SA, SB, PA, PB);
                 step(u + 1, true, SB, SA, PB, PA);
             }
+            // vf holds unit n-1 after its step
             if (u < n_units) {
                 step(u, false, SA, SB, PA, PB);
-                finish(PB);
+                value(o, vf, PB);
             } else {
-                finish(PA);
+                value(o, vf, PA);
             }
         }
         store_rows(o, m, l);
