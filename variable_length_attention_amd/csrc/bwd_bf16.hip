@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     const int64_t q_stride = (int64_t)H * D, kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
 
-    QueuePlan plan{0, 0, 0};
+    QueuePlan plan{0, 0, 0, 0};
     if (wave == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane, args.T);
 
     for (;;) {
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     const int64_t q_stride = (int64_t)H * D, kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
 
-    QueuePlan plan{0, 0, 0};
+    QueuePlan plan{0, 0, 0, 0};
     if (wave == 0) plan = queue_plan(args.cu, args.n_seq, kKeyTile, nhbq, lane, args.T);
 
     for (;;) {

@@ -44,18 +44,38 @@ __device__ inline float xhalf_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ inline int wave_sum(int x) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+// Whole-wave integer reductions, returned as a uniform value: DPP moves reduce each row of 16
+// lanes (swap neighbours, swap pairs, mirror halves, mirror the row), then the four row results
+// are read out as scalars.  No LDS round trips.
+__device__ inline int row16_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);   // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);   // row_mirror
     return x;
 }
-__device__ inline int wave_max(int x) {
-    for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+__device__ inline int row16_max(int x) {
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
     return x;
+}
+__device__ inline int wave_sum(int x) {
+    x = row16_sum(x);
+    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+           __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+__device__ inline int wave_max(int x) {
+    x = row16_max(x);
+    return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 // Two floats to two bf16 (round to nearest even) in one dword, first in the low half.
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -85,16 +105,20 @@ struct QueuePlan {
     int total;   // items in this queue
     int maxc;    // highest level
     int Tc;      // clamped token count
+    int nt0;     // tile count of sequence `lane` (0 past n_seq): the first 64 sequences stay in
+                 // registers, so decoding touches memory only for sequences 64 and up
 };
 
+__device__ inline int seq_tiles(const int32_t* cu, int i, int Tc, int W) {
+    int a, len;
+    seq_span(cu, i, Tc, a, len);
+    return (len + W - 1) / W;
+}
+
 // sum_i max(0, ntiles_i - c)
-__device__ inline int levels_above(const int32_t* cu, int n_seq, int Tc, int W, int c, int lane) {
-    int acc = 0;
-    for (int i = lane; i < n_seq; i += 64) {
-        int a, len;
-        seq_span(cu, i, Tc, a, len);
-        acc += max(0, (len + W - 1) / W - c);
-    }
+__device__ inline int levels_above(const int32_t* cu, int n_seq, const QueuePlan& p, int W, int c, int lane) {
+    int acc = max(0, p.nt0 - c);
+    for (int i = lane + 64; i < n_seq; i += 64) acc += max(0, seq_tiles(cu, i, p.Tc, W) - c);
     return wave_sum(acc);
 }
 
@@ -103,11 +127,10 @@ __device__ inline QueuePlan queue_plan(const int32_t* cu, int n_seq, int W, int 
                                        int Tbound = 0x7fffffff) {
     QueuePlan p;
     p.Tc = min(max(cu[n_seq], 0), Tbound);
-    int sum = 0, mx = 0;
-    for (int i = lane; i < n_seq; i += 64) {
-        int a, len;
-        seq_span(cu, i, p.Tc, a, len);
-        const int nt = (len + W - 1) / W;
+    p.nt0 = lane < n_seq ? seq_tiles(cu, lane, p.Tc, W) : 0;
+    int sum = p.nt0, mx = p.nt0;
+    for (int i = lane + 64; i < n_seq; i += 64) {
+        const int nt = seq_tiles(cu, i, p.Tc, W);
         sum += nt;
         mx = max(mx, nt);
     }
@@ -123,22 +146,18 @@ __device__ inline bool queue_decode(const int32_t* cu, int n_seq, const QueuePla
     int lo = 1, hi = p.maxc;   // smallest level with levels_above(level) * nhbq <= k
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (levels_above(cu, n_seq, p.Tc, W, mid, lane) * nhbq <= k) hi = mid;
+        if (levels_above(cu, n_seq, p, W, mid, lane) * nhbq <= k) hi = mid;
         else lo = mid + 1;
     }
     c = lo;
-    const int j = k - levels_above(cu, n_seq, p.Tc, W, c, lane) * nhbq;
+    const int j = k - levels_above(cu, n_seq, p, W, c, lane) * nhbq;
     int r = j / nhbq;
     hbq = j % nhbq;
     int seq = -1;
     for (int i0 = 0; i0 < n_seq && seq < 0; i0 += 64) {
         const int i = i0 + lane;
         bool ok = false;
-        if (i < n_seq) {
-            int sa, sl;
-            seq_span(cu, i, p.Tc, sa, sl);
-            ok = (sl + W - 1) / W >= c;
-        }
+        if (i < n_seq) ok = (i0 == 0 ? p.nt0 : seq_tiles(cu, i, p.Tc, W)) >= c;
         const uint64_t m = __ballot(ok);
         const int cnt = __popcll(m);
         if (r < cnt) {

@@ -54,6 +54,7 @@ constexpr int kItemRowHeads = 256;    // query (row, head) pairs per item
 constexpr int kUnit = 32;             // keys per pipeline step
 constexpr int kStage = 64;            // keys per LDS stage
 constexpr int kStages = 3;            // LDS ring depth
+constexpr int kStageRowBytes = 256;   // output staging tile row
 constexpr float kLazySum = 256.0f;    // rescale when a lane's unit sum of P exceeds 2^8
 
 template <int D>
@@ -71,6 +72,7 @@ template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][C::kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char obuf[kWaves][32 * kStageRowBytes];
     __shared__ int s_item[8];
 
     const int tid = threadIdx.x;
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     const float c2 = args.scale_log2;
 
     // ---- per-launch queue plan (wave 0 only) ----
-    QueuePlan plan{0, 0, 0};
+    QueuePlan plan{0, 0, 0, 0};
     if (wave == 0) {
         if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane);
         else plan.total = ((args.Lq + W - 1) / W) * nhbq;
@@ -131,41 +133,51 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         for (int j = 0; j < 2; ++j) vofs[j] = tr_row * C::kRowBytes + 16 * ((4 * j) ^ t) + tr_sub;
     }
 
-    for (;;) {
-        // ---- pop and decode the next item (wave 0) ----
-        if (wave == 0) {
-            int k = 0;
-            if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
-            k = __shfl(k, 0);
-            int a = 0, len = 0, hbq = 0, c = 0;
-            bool ok = k < plan.total;
-            if (ok) {
-                if (MODE == 0) {
-                    ok = queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
-                } else {
-                    a = 0;
-                    len = args.Lq;
-                    hbq = k % nhbq;
-                    c = ((args.Lq + W - 1) / W) - k / nhbq;
-                }
-            }
-            if (lane == 0) {
-                s_item[0] = ok ? a : -1;
-                s_item[1] = len;
-                s_item[2] = queue + nq_queues * hbq;
-                s_item[3] = c - 1;                 // query tile group: cost grows with it
+    // ---- item queue (wave 0) ----
+    // Item k of this workgroup's queue -> s_item[slot].  The next index is popped when an item
+    // starts and decoded when it ends, so neither the atomic's latency nor the decode sits
+    // between items; two slots, because a slow wave may still read the current item's slot.
+    auto publish = [&](int k, int slot) {
+        int a = 0, len = 0, hbq = 0, c = 0;
+        bool ok = k < plan.total;
+        if (ok) {
+            if (MODE == 0) {
+                ok = queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
+            } else {
+                a = 0;
+                len = args.Lq;
+                hbq = k % nhbq;
+                c = ((args.Lq + W - 1) / W) - k / nhbq;
             }
         }
-        __syncthreads();
+        if (lane == 0) {
+            s_item[4 * slot + 0] = ok ? a : -1;
+            s_item[4 * slot + 1] = len;
+            s_item[4 * slot + 2] = queue + nq_queues * hbq;
+            s_item[4 * slot + 3] = c - 1;                 // query tile group: cost grows with it
+        }
+    };
+    auto pop = [&]() {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
+        return k;
+    };
+    if (wave == 0) publish(__shfl(pop(), 0), 0);
+    __syncthreads();
+
+    for (int it = 0;; ++it) {
+        const int slot = it & 1;
+        int k_next = 0;
         // item fields are uniform: keep them in scalar registers
-        const int it_a = __builtin_amdgcn_readfirstlane(s_item[0]);
+        const int it_a = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
         if (it_a < 0) break;
+        if (wave == 0) k_next = pop();
         const int64_t qbase = it_a;
         const int64_t kbase = MODE == 0 ? qbase : 0;
-        const int s_rows = __builtin_amdgcn_readfirstlane(s_item[1]);
+        const int s_rows = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
         const int sk = MODE == 0 ? s_rows : args.Lk;
-        const int hb = __builtin_amdgcn_readfirstlane(s_item[2]);
-        const int tg = __builtin_amdgcn_readfirstlane(s_item[3]);
+        const int hb = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 2]);
+        const int tg = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 3]);
         // query position minus key position of (row 0, key 0)
         const int delta = MODE == 0 ? 0 : args.delta;
         const bool causal = MODE == 0 ? true : (args.causal != 0);
@@ -343,43 +355,61 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
             __syncthreads();
         };
-        // normalise and write this wave's rows
+        // Normalise and write this wave's rows.  The accumulator holds each row split over two
+        // lanes in 4-element pieces, so it goes out through a per-wave LDS tile: written there in
+        // fragment order, read back so that consecutive lanes cover whole output rows, and stored
+        // with 16-byte stores that fill complete cache lines.  A tile is 32 rows x 256 bytes (the
+        // output row, or half of it for fp32 at D = 128), slots XOR-swizzled by the row.
         auto store_rows = [&](const f32x16 (&oo)[C::kMT][kNT], const float (&mm)[kNT], const float (&ll)[kNT]) {
             if (!wave_rows) return;
+            constexpr int kE = MODE == 0 ? 2 : 4;                  // output element bytes
+            constexpr int kOutRow = D * kE;
+            constexpr int kWb = kOutRow < kStageRowBytes ? kOutRow : kStageRowBytes;
+            constexpr int kNB = kOutRow / kWb;                     // column blocks per row
+            constexpr int kSlots = kWb / 16;                       // 16-byte slots per tile row
+            constexpr int kRowsPerRead = 64 / kSlots;
+            unsigned char* tile = obuf[wave];
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 const float lt = xhalf_sum(ll[nt]);
                 const float inv = lt > 0.f ? 1.f / lt : 0.f;
                 const float mb = (mm[nt] == -INFINITY) ? 0.f : mm[nt];
                 const float lse = lt > 0.f ? (mb + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-                const int row = r_lo + nt * 32 + l32;
-                if (row < s_rows) {
-                    const int64_t orow = (qbase + row) * (int64_t)H + head;
-                    if (MODE == 0) {
-                        uint16_t* op = (uint16_t*)args.out + orow * D;
+                const int row0 = r_lo + nt * 32;                   // first row of this tile
+                if (half == 0 && row0 + l32 < s_rows) args.lse[(qbase + row0 + l32) * (int64_t)H + head] = lse;
 #pragma unroll
-                        for (int mt = 0; mt < C::kMT; ++mt)
+                for (int b = 0; b < kNB; ++b) {
+                    // fragment -> tile: lane (row l32, half) holds d = mt*32 + 8*a4 + 4*half + 0..3
 #pragma unroll
-                            for (int a4 = 0; a4 < 4; ++a4) {
-                                const int d0 = mt * 32 + 8 * a4 + 4 * half;
+                    for (int mt = 0; mt < C::kMT; ++mt) {
+                        if (mt * 32 * kE < b * kWb || mt * 32 * kE >= (b + 1) * kWb) continue;
+#pragma unroll
+                        for (int a4 = 0; a4 < 4; ++a4) {
+                            const int byte = (mt * 32 + 8 * a4 + 4 * half) * kE - b * kWb;
+                            unsigned char* dst = tile + l32 * kWb + (((byte >> 4) ^ (l32 % kSlots)) << 4) + (byte & 15);
+                            const float x0 = oo[mt][nt][4 * a4 + 0] * inv, x1 = oo[mt][nt][4 * a4 + 1] * inv;
+                            const float x2 = oo[mt][nt][4 * a4 + 2] * inv, x3 = oo[mt][nt][4 * a4 + 3] * inv;
+                            if (MODE == 0) {
                                 u32x2 w;
-                                w[0] = pack_bf16x2(oo[mt][nt][4 * a4 + 0] * inv, oo[mt][nt][4 * a4 + 1] * inv);
-                                w[1] = pack_bf16x2(oo[mt][nt][4 * a4 + 2] * inv, oo[mt][nt][4 * a4 + 3] * inv);
-                                *(u32x2*)(op + d0) = w;
+                                w[0] = pack_bf16x2(x0, x1);
+                                w[1] = pack_bf16x2(x2, x3);
+                                *(u32x2*)dst = w;
+                            } else {
+                                *(float4*)dst = make_float4(x0, x1, x2, x3);
                             }
-                    } else {
-                        float* op = (float*)args.out + orow * D;
-#pragma unroll
-                        for (int mt = 0; mt < C::kMT; ++mt)
-#pragma unroll
-                            for (int a4 = 0; a4 < 4; ++a4) {
-                                const int d0 = mt * 32 + 8 * a4 + 4 * half;
-                                float4 w = make_float4(oo[mt][nt][4 * a4 + 0] * inv, oo[mt][nt][4 * a4 + 1] * inv,
-                                                       oo[mt][nt][4 * a4 + 2] * inv, oo[mt][nt][4 * a4 + 3] * inv);
-                                *(float4*)(op + d0) = w;
-                            }
+                        }
                     }
-                    if (half == 0) args.lse[orow] = lse;
+                    // tile -> global: lane i covers slot i % kSlots of tile row i / kSlots (+ step)
+#pragma unroll
+                    for (int rr = 0; rr < 32; rr += kRowsPerRead) {
+                        const int tr = rr + lane / kSlots, slot = lane % kSlots;
+                        const u32x4 val = *(const u32x4*)(tile + tr * kWb + ((slot ^ (tr % kSlots)) << 4));
+                        if (row0 + tr < s_rows) {
+                            unsigned char* gp = (unsigned char*)args.out +
+                                                ((qbase + row0 + tr) * (int64_t)H + head) * kOutRow + b * kWb + slot * 16;
+                            *(u32x4*)gp = val;
+                        }
+                    }
                 }
             }
         };
@@ -523,6 +553,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
         }
         store_rows(o, m, l);
+        if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();
     }
 
