@@ -31,12 +31,17 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_packed_slice_8k.json")
-FWD_SRC = os.path.join(ROOT, "variable_length_attention_amd", "csrc", "fwd_bf16.hip")
+# the forward kernel's sources: counters taken on another version of them do not apply
+FWD_SRC = [os.path.join(ROOT, "variable_length_attention_amd", "csrc", f)
+           for f in ("fwd_bf16.hip", "device_common.h", "hdp_internal.h")]
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic():

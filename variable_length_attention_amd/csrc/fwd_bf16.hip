@@ -480,7 +480,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             constexpr int kQK = C::kKS * kNT;
             constexpr int kElems = 16 * kNT;                       // score elements per lane
             constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
-            float mb[kNT], ls[kNT], lb[kNT];
+            float mb[kNT], ls[kNT], lb[kNT], pe = 0.f;
+            uint32_t pw[kNT][8];                                   // P as bf16 pairs
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 mb[nt] = (m[nt] == -INFINITY) ? 0.f : m[nt];
@@ -508,18 +509,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 if (k < kElems) {
                     const int nt = k / 16, i = k % 16;
                     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[nt][i], c2, -mb[nt]));
-                    ls[nt] += pv;
-                    Pc[nt][i >> 3][i & 7] = (__bf16)pv;
+                    ls[nt] = i == 0 ? pv : ls[nt] + pv;
+                    if (i & 1) {
+                        // pack the pair in this slot; the empty asm anchors the conversion here
+                        // (otherwise it drifts to the end of the step, or into the rare branch)
+                        pw[nt][i >> 1] = pack_bf16x2(pe, pv);
+                        asm volatile("" : "+v"(pw[nt][i >> 1]));
+                    } else {
+                        pe = pv;
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) l[nt] += ls[nt];
-            // Pin this step's softmax results here, so the compiler cannot sink them into the
-            // no-rescale side of the rare branch below.
-#pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                asm volatile("" : "+v"(Pc[nt][0]), "+v"(Pc[nt][1]), "+v"(l[nt]));
+                l[nt] += ls[nt];
+                asm volatile("" : "+v"(l[nt]));
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    Pc[nt][h] = __builtin_bit_cast(bf16x8, u32x4{pw[nt][4 * h], pw[nt][4 * h + 1], pw[nt][4 * h + 2],
+                                                                 pw[nt][4 * h + 3]});
             }
             fix_rescale(Sc, Pc, ls, lb);
             if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
