@@ -272,7 +272,7 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     if ((int64_t)T * H > (int64_t)INT32_MAX) return HDP_ERR_OVERFLOW;
     DeviceState* st = nullptr;
     if (int rc = device_state(&st)) return rc;
-    if (int rc = ensure_workspace(st, sizeof(float) * (size_t)T * (size_t)H)) return rc;
+    if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)T * (size_t)H)) return rc;
     hdp::BwdArgs a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -287,7 +287,7 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     a.Hkv = Hkv;
     a.scale = scale;
     a.scale_log2 = scale * kLog2e;
-    a.delta = (float*)st->ws;
+    a.rowvals = (float*)st->ws;
     a.dq = (uint16_t*)dq;
     a.dk = (uint16_t*)dk;
     a.dv = (uint16_t*)dv;

@@ -12,12 +12,14 @@
 //         S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
 //     Rows live in lanes (as in the forward), so lse and delta are one value per lane and dS^T
 //     is already the B operand of the last product; K^T comes from transposing LDS reads.  It
-//     also computes delta from dO and O and writes it for the second kernel.
+//     also computes delta from dO and O and writes it, with lse in log2 units, head-major
+//     ([2][H][T]: rows of one head contiguous) for the second kernel.
 //   * dK/dV kernel, key-major (one item = 128 keys of one key/value head, 32 keys per wave):
 //         S = Q K^T,  dP = dO V^T,  dS = P * (dP - delta),  dV += P^T dO,  dK += dS^T Q,
 //     for every 32-row unit of the sequence at or after the keys and every query head of the
 //     group.  Keys live in lanes, so P and dS are directly the A operands of the two
-//     accumulating products; dO and Q come from transposing LDS reads.
+//     accumulating products; dO and Q come from transposing LDS reads.  Software-pipelined
+//     like the forward (see the kernel).
 // The score products are recomputed in both kernels (seven products per pair instead of five):
 // the price of keeping dS out of memory and dQ free of atomics.
 #include "device_common.h"
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         }
         const float delta = xhalf_sum(dpart);
         const float lse2 = row_ok ? args.lse[(base + row) * H + head] * kLog2e : 0.f;
-        if (row_ok && half == 0) args.delta[(base + row) * H + head] = delta;
+        if (row_ok) args.rowvals[((int64_t)half * H + head) * args.T + base + row] = half == 0 ? lse2 : delta;
 
         f32x16 acc[C::kMT];
 #pragma unroll
@@ -254,13 +256,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
 // =============================================================================================
 // dK/dV kernel
 // =============================================================================================
+// Item = 128 keys of one key/value head (wave w owns keys 32w..32w+31 of the tile, as the B
+// operand: K^T and V^T fragments stay in registers).  Its steps walk the stages (row unit of 32
+// rows, query head of the group) from the diagonal to the end of the sequence.  Step st issues
+// the dV/dK products of stage st-1 (16 MFMAs) and the S/dP products of stage st+1 (16 MFMAs)
+// around the elementwise part of stage st (P = exp2(S c - lse2), dS = P (dP - delta)), one
+// element per slot.  Q and dO tiles (32 rows each) and the stage's 32 lse2 and delta values
+// arrive in LDS through direct global->LDS loads, in a ring of four stages two steps ahead.
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     using C = Cfg<D>;
-    constexpr int kTile = kUnit * C::kRowBytes;     // 32 rows of Q or dO
-    constexpr int kBlocks = kUnit / C::kRowsPerBlock;   // 1 KB loads per tile
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][kTile];
-    __shared__ int s_item[4];
+    constexpr int kTile = kUnit * C::kRowBytes;           // 32 rows of Q or dO
+    constexpr int kBlocks = kUnit / C::kRowsPerBlock;      // 1 KB loads per tile
+    constexpr int kBPW = kBlocks / kWaves;                 // per wave
+    constexpr int kRing = 4;
+    constexpr int kLoadsPerStage = 2 * kBPW + 1;          // vector memory ops per stage, per wave
+    struct Stage {
+        unsigned char q[kTile];
+        unsigned char d[kTile];
+        float rv[2][kUnit];                                // lse2, delta of the 32 rows
+    };
+    __shared__ __attribute__((aligned(1024))) Stage ring[kRing];
+    __shared__ int s_item[8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -272,35 +289,68 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     const int queue = blockIdx.x % args.nqueues_kv;
     const int64_t q_stride = (int64_t)H * D, kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
+    const int Trv = args.T;                                // row stride of the lse2/delta planes
+
+    // per-lane LDS offsets: row fragments (A operand: row l32, slot (2ks+half)^swz), transposed
+    // fragments (B operand over 16 rows x 32 columns, as the forward's V^T reads), stage loads
+    int rofs[4];
+    {
+        const int t = half ^ swz(l32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rofs[j] = l32 * C::kRowBytes + 16 * ((2 * j) ^ t);
+    }
+    const int gidx = lane >> 4;
+    const int tr_row = 4 * (gidx >> 1) + ((lane & 15) >> 2);
+    const int tr_col = 16 * (gidx & 1) + 4 * (lane & 3);
+    int tofs[2];
+    {
+        const int t = (tr_col >> 3) ^ swz(tr_row);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) tofs[j] = tr_row * C::kRowBytes + 16 * ((4 * j) ^ t) + (lane & 1) * 8;
+    }
+    int grow[kBPW], gchunk[kBPW];
+#pragma unroll
+    for (int i = 0; i < kBPW; ++i) {
+        grow[i] = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
+        gchunk[i] = (lane % C::kChunks) ^ swz(grow[i]);
+    }
 
     QueuePlan plan{0, 0, 0, 0};
     if (wave == 0) plan = queue_plan(args.cu, args.n_seq, kKeyTile, nhbq, lane, args.T);
-
-    for (;;) {
-        if (wave == 0) {
-            int k = 0;
-            if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
-            k = __shfl(k, 0);
-            int a = 0, len = 0, hbq = 0, c = 0;
-            const bool ok = k < plan.total &&
-                            queue_decode(args.cu, args.n_seq, plan, kKeyTile, nhbq, k, lane, a, len, hbq, c);
-            if (lane == 0) {
-                s_item[0] = ok ? a : -1;
-                s_item[1] = len;
-                s_item[2] = queue + args.nqueues_kv * hbq;
-                // level c = tiles from this one to the end: earlier key tiles see more rows
-                s_item[3] = (len + kKeyTile - 1) / kKeyTile - c;
-            }
+    auto publish = [&](int k, int slot) {
+        int a = 0, len = 0, hbq = 0, c = 0;
+        const bool ok = k < plan.total && queue_decode(args.cu, args.n_seq, plan, kKeyTile, nhbq, k, lane, a, len, hbq, c);
+        if (lane == 0) {
+            s_item[4 * slot + 0] = ok ? a : -1;
+            s_item[4 * slot + 1] = len;
+            s_item[4 * slot + 2] = queue + args.nqueues_kv * hbq;
+            // level c = tiles from this one to the end: earlier key tiles see more rows
+            s_item[4 * slot + 3] = (len + kKeyTile - 1) / kKeyTile - c;
         }
-        __syncthreads();
-        const int a0 = __builtin_amdgcn_readfirstlane(s_item[0]);
+    };
+    auto pop = [&]() {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
+        return k;
+    };
+    if (wave == 0) publish(__shfl(pop(), 0), 0);
+    __syncthreads();
+
+    for (int it = 0;; ++it) {
+        const int slot = it & 1;
+        const int a0 = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
         if (a0 < 0) break;
+        int k_next = 0;
+        if (wave == 0) k_next = pop();
         const int64_t base = a0;
-        const int s = __builtin_amdgcn_readfirstlane(s_item[1]);
-        const int g = __builtin_amdgcn_readfirstlane(s_item[2]);
-        const int kt = __builtin_amdgcn_readfirstlane(s_item[3]);
+        const int s = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
+        const int g = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 2]);
+        const int kt = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 3]);
         const int kj0 = kt * kKeyTile + wave * kUnit;   // this wave's first key
         const int key = kj0 + l32;                      // this lane's key (B-operand column)
+        const int ru0 = kt * (kKeyTile / kUnit);
+        const int n_ru = (s + kUnit - 1) / kUnit;
+        const int n_st = (n_ru - ru0) * G;              // stages (row unit, head)
 
         // K^T and V^T fragments of this wave's 32 keys
         u32x4 kf[C::kKS], vf[C::kKS];
@@ -313,109 +363,239 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
                 vf[ks] = ok ? *(const u32x4*)(args.v + off + ks * 16) : u32x4{0, 0, 0, 0};
             }
         }
+
+        // stage st -> ring buffer st % 4: Q and dO rows (clamped into the sequence) and the
+        // rows' lse2 / delta (one 4-byte lane load each; lanes 0-31 lse2, 32-63 delta)
+        auto load_stage = [&](int st) {
+            const int ru = ru0 + st / G, hh = st % G;
+            const int head = g * G + hh;
+            const int r0 = ru * kUnit;
+            Stage& S = ring[st % kRing];
+#pragma unroll
+            for (int i = 0; i < kBPW; ++i) {
+                const int blk = wave * kBPW + i;
+                const int64_t off = (base + min(r0 + grow[i], s - 1)) * q_stride + (int64_t)head * D + gchunk[i] * 8;
+                __builtin_amdgcn_global_load_lds(args.q + off, (lds_void*)(S.q + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(args.dout + off, (lds_void*)(S.d + blk * 1024), 16, 0, 0);
+            }
+            {   // every wave loads the same 256 bytes, so all count the same memory ops
+                const int64_t r = base + min(r0 + l32, s - 1);
+                const float* src = args.rowvals + ((int64_t)half * H + head) * Trv + r;
+                __builtin_amdgcn_global_load_lds(src, (lds_void*)&S.rv[0][0], 4, 0, 0);
+            }
+        };
+        auto tile_base = [&](int st, int which) {   // uniform LDS address of a stage's tile
+            Stage& S = ring[st % kRing];
+            return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(which == 0 ? S.q : S.d));
+        };
+        // A-operand row fragments of a tile (Q or dO rows), k-steps ks0 .. ks0 + n - 1 over D
+        auto read_rows = [&](int st, int which, u32x4 (&f)[C::kKS], int ks0, int n) {
+            const uint32_t b = tile_base(st, which);
+            uint32_t a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = lds_add(b, rofs[j]);
+#pragma unroll
+            for (int ks = 0; ks < C::kKS; ++ks)
+                if (ks >= ks0 && ks < ks0 + n) f[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
+        };
+        // B-operand transposed fragments: for k-step ks2 and D tile mt, lane l receives column
+        // mt*32 + l%32 of rows 16 ks2 + 8 (i/4) + 4 (l/32) + i%4 (the accumulator row order)
+        auto read_cols = [&](int st, int which, bf16x8 (&f)[2][C::kMT]) {
+            const uint32_t b = tile_base(st, which);
+            const uint32_t a[2] = {lds_add(b, tofs[0]), lds_add(b, tofs[1])};
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt) {
+                    const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
+                    f[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
+                    f[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
+                }
+        };
+        // lse2 and delta of the lane's accumulator rows 8*j + 4*half + (0..3) (elements 4j..4j+3)
+        auto read_rowvals = [&](int st, int j, f32x4& l2, f32x4& dl) {
+            const Stage& S = ring[st % kRing];
+            l2 = *(const f32x4*)&S.rv[0][8 * j + 4 * half];
+            dl = *(const f32x4*)&S.rv[1][8 * j + 4 * half];
+        };
+        // S (rows x keys) = Q K^T and dP = dO V^T of one stage from its row fragments
+        auto sdp_full = [&](const u32x4 (&qr)[C::kKS], const u32x4 (&dr)[C::kKS], f32x16& S, f32x16& dP) {
+            S = f32x16{};
+            dP = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < C::kKS; ++ks) {
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qr[ks]), __builtin_bit_cast(bf16x8, kf[ks]), S, 0, 0, 0);
+                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[ks]), __builtin_bit_cast(bf16x8, vf[ks]), dP, 0, 0, 0);
+            }
+        };
+        // invisible (key, row) pairs of stage st get S = -inf, so P = 0 and dS = 0
+        auto stage_full = [&](int st) {
+            const int r0 = (ru0 + st / G) * kUnit;
+            return kt * kKeyTile + kKeyTile - 1 <= r0 && r0 + kUnit <= s;
+        };
+        auto apply_mask = [&](int st, f32x16& S) {
+            const int r0 = (ru0 + st / G) * kUnit;
+            const int lim = min(s - 1 - r0, kUnit);     // rows r0 + jr with jr <= lim exist
+            const int kr = key - r0;                    // visible iff jr >= kr
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int jr = 8 * (i >> 2) + 4 * half + (i & 3);
+                S[i] = (jr < kr || jr > lim) ? -INFINITY : S[i];
+            }
+        };
+
         f32x16 dk[C::kMT], dv[C::kMT];
 #pragma unroll
         for (int mt = 0; mt < C::kMT; ++mt) { dk[mt] = f32x16{}; dv[mt] = f32x16{}; }
 
-        // stages: (row unit ru, head hh) for ru = ru0 .. n_ru-1, hh = 0 .. G-1
-        const int ru0 = kt * (kKeyTile / kUnit);
-        const int n_ru = (s + kUnit - 1) / kUnit;
-        const int n_stages = (n_ru - ru0) * G;
-        auto load_stage = [&](int st) {
-            const int ru = ru0 + st / G, hh = st % G;
-            const int head = g * G + hh;
-            unsigned char* qb = smem[st % kStages][0];
-            unsigned char* db = smem[st % kStages][1];
-#pragma unroll
-            for (int i = 0; i < kBlocks / kWaves; ++i) {
-                const int blk = wave * (kBlocks / kWaves) + i;
-                dma_block<D>(args.q + (int64_t)head * D, q_stride, base + ru * kUnit, s - 1 - ru * kUnit, blk, lane, qb);
-                dma_block<D>(args.dout + (int64_t)head * D, q_stride, base + ru * kUnit, s - 1 - ru * kUnit, blk, lane, db);
-            }
-        };
-        // lse (log2 units) and delta of the lane's 16 accumulator rows 8*(i/4) + 4*half + (i%4)
-        auto load_rowvals = [&](int st, float (&l2)[16], float (&dl)[16]) {
-            const int ru = ru0 + st / G, hh = st % G;
-            const int head = g * G + hh;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = ru * kUnit + 8 * (i >> 2) + 4 * half + (i & 3);
-                const int rc = min(r, s - 1);
-                const int64_t o = (base + rc) * H + head;
-                l2[i] = args.lse[o] * kLog2e;
-                dl[i] = args.delta[o];
-            }
-        };
-
-        if (n_stages > 0) {
+        if (n_st > 0) {
+            // prologue: stages 0..2 in flight, stage 0 scored
             load_stage(0);
-            if (n_stages > 1) load_stage(1);
-        }
-        float l2[16], dl[16];
-        if (n_stages > 0) load_rowvals(0, l2, dl);
-        wait_vm0();
-        __syncthreads();
-
-        for (int st = 0; st < n_stages; ++st) {
-            if (st + 2 < n_stages) load_stage(st + 2);
-            const int ru = ru0 + st / G;
-            const int r0 = ru * kUnit;
-            if (kj0 <= r0 + kUnit - 1) {                 // some key of this wave is visible
-                const unsigned char* qb = smem[st % kStages][0];
-                const unsigned char* db = smem[st % kStages][1];
-                u32x4 qr[C::kKS], dr[C::kKS];
-                lds_rows_frag<D>(qb, l32, half, qr);
-                lds_rows_frag<D>(db, l32, half, dr);
-                f32x16 S = f32x16{}, dP = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < C::kKS; ++ks) {
-                    S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qr[ks]),
-                                                                __builtin_bit_cast(bf16x8, kf[ks]), S, 0, 0, 0);
-                    dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[ks]),
-                                                                 __builtin_bit_cast(bf16x8, vf[ks]), dP, 0, 0, 0);
-                }
-                // S[i]: row r0 + 8*(i/4) + 4*half + (i%4), key = this lane's key
-                const bool full = kj0 + kUnit - 1 <= r0 && r0 + kUnit <= s;
-                bf16x8 pb[2], sb[2];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = r0 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    const bool vis = full || (key <= r && r < s);
-                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -l2[i])) : 0.f;
-                    pb[i >> 3][i & 7] = (__bf16)p;
-                    sb[i >> 3][i & 7] = (__bf16)(p * (dP[i] - dl[i]));
-                }
-                bf16x8 dt[2][C::kMT], qt[2][C::kMT];
-                lds_cols_frag<D>(db, 0, lane, dt);
-                lds_cols_frag<D>(qb, 0, lane, qt);
-#pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-                    for (int mt = 0; mt < C::kMT; ++mt) {
-                        dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[ks2], dt[ks2][mt], dv[mt], 0, 0, 0);
-                        dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[ks2], qt[ks2][mt], dk[mt], 0, 0, 0);
-                    }
-            }
-            if (st + 1 < n_stages) load_rowvals(st + 1, l2, dl);
-            wait_vm0();
+            if (n_st > 1) load_stage(1);
+            if (n_st > 2) load_stage(2);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
+            f32x16 SA, DA, SB, DB;
+            bf16x8 PA[2], TA[2], PB[2], TB[2];       // P and dS as bf16 A operands
+            bf16x8 dt[2][C::kMT], qt[2][C::kMT];
+            {
+                u32x4 qr[C::kKS], dr[C::kKS];
+                read_rows(0, 0, qr, 0, C::kKS);
+                read_rows(0, 1, dr, 0, C::kKS);
+                sdp_full(qr, dr, SA, DA);
+            }
+            if (!stage_full(0)) apply_mask(0, SA);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) { PA[j] = bf16x8{}; TA[j] = bf16x8{}; }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt) { dt[ks2][mt] = bf16x8{}; qt[ks2][mt] = bf16x8{}; }
+
+            // step st: dV/dK of st-1 (operands Pp, Tp, dt, qt), S/dP of st+1 into Sn/Dn, the
+            // elementwise part of st from Sc/Dc into Pc/Tc
+            auto step = [&](int st, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn, const bf16x8 (&Pp)[2],
+                            const bf16x8 (&Tp)[2], bf16x8 (&Pc)[2], bf16x8 (&Tc)[2]) {
+                // stage st+1 must have landed; stage st+2 (issued one step ago) may still fly
+                if (st > 0) {
+                    if (st + 2 < n_st) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerStage);
+                    else __builtin_amdgcn_s_waitcnt(0x0F70);
+                    __syncthreads();
+                }
+                // ring buffer of stage st+3 last held stage st-1, read up to step st-1
+                if (st + 3 < n_st) load_stage(st + 3);
+                u32x4 qr[C::kKS], dr[C::kKS];
+                const int sn = min(st + 1, n_st - 1);     // past the end: harmless re-read
+                constexpr int kH = C::kKS / 2;             // second half read mid-way
+                read_rows(sn, 0, qr, 0, kH);
+                read_rows(sn, 1, dr, 0, kH);
+                __builtin_amdgcn_sched_barrier(0);
+                uint32_t pw[8], tw[8];
+                float pe = 0.f, te = 0.f;
+                f32x4 l2[2], dl[2];                        // rows of element groups j, j+1
+                read_rowvals(st, 0, l2[0], dl[0]);
+                constexpr int kDV = 2 * C::kMT;            // dV MFMAs (and as many dK MFMAs)
+                constexpr int kSlots = 4 * kDV > 32 ? 4 * kDV : 32;
+#pragma unroll
+                for (int k = 0; k < kSlots; ++k) {
+                    if (k == kDV) {
+                        read_rows(sn, 0, qr, kH, kH);
+                        read_rows(sn, 1, dr, kH, kH);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (k == 2 * kDV) {
+                        // dt/qt of st-1 consumed: read stage st's transposed fragments for st+1
+                        read_cols(st, 1, dt);
+                        read_cols(st, 0, qt);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (k < 2 * kDV) {
+                        const int j = k >> 1, ks2 = j / C::kMT, mt = j % C::kMT;
+                        if ((k & 1) == 0) dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pp[ks2], dt[ks2][mt], dv[mt], 0, 0, 0);
+                        else dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Tp[ks2], qt[ks2][mt], dk[mt], 0, 0, 0);
+                    } else if (k < 2 * kDV + 2 * C::kKS) {
+                        const int j = k - 2 * kDV, ks = j >> 1;
+                        if (j == 0) Sn = f32x16{};      // the accumulators start here (zero C operand)
+                        if (j == 1) Dn = f32x16{};
+                        if ((j & 1) == 0) Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qr[ks]), __builtin_bit_cast(bf16x8, kf[ks]), Sn, 0, 0, 0);
+                        else Dn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[ks]), __builtin_bit_cast(bf16x8, vf[ks]), Dn, 0, 0, 0);
+                    }
+                    if (k < 16 && (k & 3) == 0 && k + 4 < 16) read_rowvals(st, (k >> 2) + 1, l2[((k >> 2) + 1) & 1], dl[((k >> 2) + 1) & 1]);
+                    if (k < 16) {
+                        const int i = k, jb = (i >> 2) & 1;
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[i], c2, -l2[jb][i & 3]));
+                        const float t = p * (Dc[i] - dl[jb][i & 3]);
+                        if (i & 1) {
+                            pw[i >> 1] = pack_bf16x2(pe, p);
+                            tw[i >> 1] = pack_bf16x2(te, t);
+                            asm volatile("" : "+v"(pw[i >> 1]), "+v"(tw[i >> 1]));
+                        } else {
+                            pe = p;
+                            te = t;
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    Pc[h] = __builtin_bit_cast(bf16x8, u32x4{pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]});
+                    Tc[h] = __builtin_bit_cast(bf16x8, u32x4{tw[4 * h], tw[4 * h + 1], tw[4 * h + 2], tw[4 * h + 3]});
+                }
+                if (st + 1 < n_st && !stage_full(st + 1)) apply_mask(st + 1, Sn);
+            };
+            int st = 0;
+            for (; st + 1 < n_st; st += 2) {
+                step(st, SA, DA, SB, DB, PA, TA, PB, TB);
+                step(st + 1, SB, DB, SA, DA, PB, TB, PA, TA);
+            }
+            // the dV/dK products of the last stage (its dt/qt were read in its step)
+            const bf16x8 (&PL)[2] = (st < n_st) ? PB : PA;
+            const bf16x8 (&TL)[2] = (st < n_st) ? TB : TA;
+            if (st < n_st) step(st, SA, DA, SB, DB, PA, TA, PB, TB);
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt) {
+                    dv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(PL[ks2], dt[ks2][mt], dv[mt], 0, 0, 0);
+                    dk[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TL[ks2], qt[ks2][mt], dk[mt], 0, 0, 0);
+                }
         }
 
         // dK = scale * dk, dV = dv; accumulator element i of D tile mt is key
-        // kj0 + 8*(i/4) + 4*half + (i%4), column mt*32 + l32
+        // kj0 + 8*(i/4) + 4*half + (i%4), column mt*32 + l32.  Out through this wave's share of
+        // the ring (after every wave left the loop): rows of 32 keys, then 16-byte stores.
+        __syncthreads();
+        {
+            unsigned char* tk = ring[wave].q;           // 32 keys x D bf16 each
+            unsigned char* tv = ring[wave].d;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kr = kj0 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (kr < s) {
-                uint16_t* kp = args.dk + ((base + kr) * Hkv + g) * D + l32;
-                uint16_t* vp = args.dv + ((base + kr) * Hkv + g) * D + l32;
+            for (int i = 0; i < 16; ++i) {
+                const int kr = 8 * (i >> 2) + 4 * half + (i & 3);
 #pragma unroll
                 for (int mt = 0; mt < C::kMT; ++mt) {
-                    kp[mt * 32] = __builtin_bit_cast(uint16_t, (__bf16)(dk[mt][i] * args.scale));
-                    vp[mt * 32] = __builtin_bit_cast(uint16_t, (__bf16)dv[mt][i]);
+                    const int col = mt * 32 + l32;
+                    const int off = kr * C::kRowBytes + (((col >> 3) ^ swz(kr)) << 4) + (col & 7) * 2;
+                    *(__bf16*)(tk + off) = (__bf16)(dk[mt][i] * args.scale);
+                    *(__bf16*)(tv + off) = (__bf16)dv[mt][i];
+                }
+            }
+            constexpr int kRowsPerRead = 64 / C::kChunks;
+#pragma unroll
+            for (int rr = 0; rr < kUnit; rr += kRowsPerRead) {
+                const int kr = rr + lane / C::kChunks, ch = lane % C::kChunks;
+                const int off = kr * C::kRowBytes + ((ch ^ swz(kr)) << 4);
+                const u32x4 wk = *(const u32x4*)(tk + off);
+                const u32x4 wv = *(const u32x4*)(tv + off);
+                if (kj0 + kr < s) {
+                    const int64_t o = ((base + kj0 + kr) * Hkv + g) * D + ch * 8;
+                    *(u32x4*)(args.dk + o) = wk;
+                    *(u32x4*)(args.dv + o) = wv;
                 }
             }
         }
+        if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();
     }
     if (tid == 0) queue_finish(args.counters);

@@ -67,7 +67,8 @@ struct BwdArgs {
     int32_t H, Hkv;
     float scale;
     float scale_log2;
-    float* delta;           // [T][H] workspace: rowsum(dO * out), written by the dQ kernel
+    float* rowvals;         // [2][H][T] workspace written by the dQ kernel: lse * log2(e) and
+                            // delta = rowsum(dO * out), rows of one head contiguous
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
