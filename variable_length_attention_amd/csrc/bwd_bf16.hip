@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
 // =============================================================================================
 // Item = 128 keys of one key/value head (wave w owns keys 32w..32w+31 of the tile, as the B
 // operand: K^T and V^T fragments stay in registers).  Its steps walk the stages (row unit of 32
-// rows, query head of the group) from the diagonal to the end of the sequence.  Step st issues
+// rows, query head of the group) from the end of the sequence down to the diagonal.  Step st issues
 // the dV/dK products of stage st-1 (16 MFMAs) and the S/dP products of stage st+1 (16 MFMAs)
 // around the elementwise part of stage st (P = exp2(S c - lse2), dS = P (dP - delta)), one
 // element per slot.  Q and dO tiles (32 rows each) and the stage's 32 lse2 and delta values
@@ -350,7 +350,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         const int key = kj0 + l32;                      // this lane's key (B-operand column)
         const int ru0 = kt * (kKeyTile / kUnit);
         const int n_ru = (s + kUnit - 1) / kUnit;
-        const int n_st = (n_ru - ru0) * G;              // stages (row unit, head)
+        // stages (row unit, head), row units from the last one down to the key tile's diagonal:
+        // the items of one key/value head start together at the sequence's end and move down
+        // in step, so the workgroups of an XCD read the same Q/dO rows through its L2
+        const int n_st = (n_ru - ru0) * G;
 
         // K^T and V^T fragments of this wave's 32 keys
         u32x4 kf[C::kKS], vf[C::kKS];
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         // stage st -> ring buffer st % 4: Q and dO rows (clamped into the sequence) and the
         // rows' lse2 / delta (one 4-byte lane load each; lanes 0-31 lse2, 32-63 delta)
         auto load_stage = [&](int st) {
-            const int ru = ru0 + st / G, hh = st % G;
+            const int ru = n_ru - 1 - st / G, hh = st % G;
             const int head = g * G + hh;
             const int r0 = ru * kUnit;
             Stage& S = ring[st % kRing];
@@ -432,11 +435,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         };
         // invisible (key, row) pairs of stage st get S = -inf, so P = 0 and dS = 0
         auto stage_full = [&](int st) {
-            const int r0 = (ru0 + st / G) * kUnit;
+            const int r0 = (n_ru - 1 - st / G) * kUnit;
             return kt * kKeyTile + kKeyTile - 1 <= r0 && r0 + kUnit <= s;
         };
         auto apply_mask = [&](int st, f32x16& S) {
-            const int r0 = (ru0 + st / G) * kUnit;
+            const int r0 = (n_ru - 1 - st / G) * kUnit;
             const int lim = min(s - 1 - r0, kUnit);     // rows r0 + jr with jr <= lim exist
             const int kr = key - r0;                    // visible iff jr >= kr
 #pragma unroll
