@@ -57,6 +57,9 @@ def _load():
     lib.orc_varlen_bwd.argtypes = [P, P, P, P, P, i64, i32, i32, i32, f64, P, i64, P, i64, P, P,
                                    P, i32]
     lib.orc_varlen_bwd.restype = i32
+    lib.orc_chunk_bwd.argtypes = [P, i64, P, P, i64, i64, i64, i32, i32, i32, i32, f64, P, P, P, P,
+                                  P, P, i32]
+    lib.orc_chunk_bwd.restype = i32
     lib.orc_count_pairs.argtypes = [i64, i64, i64, i64, i32]
     lib.orc_count_pairs.restype = ctypes.c_uint64
     lib.orc_attn_flops.argtypes = [i64, i64, i64, i64, i32, i32, i32, i32]
@@ -167,6 +170,26 @@ def varlen_bwd(q, k, v, dout, cu_seqlens, scale, qrows=None, krows=None, nthread
                             _ptr(dv), int(nthreads))
     if st != ORC_OK:
         raise ValueError("orc_varlen_bwd failed with status %d" % st)
+    return dq, dk, dv
+
+
+def chunk_bwd(q_slice, k_chunk, v_chunk, q_offset, kv_offset, causal, scale, out, lse, dout,
+              nthreads=0):
+    """One ring step of the backward, given the slice's final out [Lq,H,D] and lse [Lq,H]:
+    returns this chunk's share (dq [Lq,H,D], dk [Lk,Hkv,D], dv [Lk,Hkv,D]) in fp64."""
+    lib = _load()
+    q, k, v = _f64(q_slice), _f64(k_chunk), _f64(v_chunk)
+    o, l, do = _f64(out), _f64(lse), _f64(dout)
+    Lq, H, D = q.shape
+    Lk, Hkv = k.shape[0], k.shape[1]
+    dq = np.zeros((Lq, H, D), np.float64)
+    dk = np.zeros((Lk, Hkv, D), np.float64)
+    dv = np.zeros((Lk, Hkv, D), np.float64)
+    st = lib.orc_chunk_bwd(_ptr(q), Lq, _ptr(k), _ptr(v), Lk, int(q_offset), int(kv_offset),
+                           int(bool(causal)), H, Hkv, D, float(scale), _ptr(o), _ptr(l), _ptr(do),
+                           _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+    if st != ORC_OK:
+        raise ValueError("orc_chunk_bwd failed with status %d" % st)
     return dq, dk, dv
 
 

@@ -204,6 +204,89 @@ int orc_chunk_partial(const double* q, int64_t Lq, const double* k, const double
 }
 
 /*
+ * One ring step of the backward (the backward counterpart of orc_chunk_partial): the slice's
+ * rows (Lq tokens at global positions q_offset + r) against one key/value chunk (Lk tokens at
+ * kv_offset + j), given the slice's final output `out` and lse over the whole key range, and
+ * dO.  Same visibility as orc_chunk_partial.  With P_rj = exp(scale <q_r, k_j> - lse_r) and
+ * delta_r = sum_d dO_r[d] out_r[d] (the chain rule of the definition above, summed over this
+ * chunk's keys only):
+ *     dq_r = scale sum_j P_rj (<dO_r, v_j> - delta_r) k_j          this chunk's share of dQ
+ *     dk_j = scale sum_{h in group} sum_r P_rj (<dO_r, v_j> - delta_r) q_r
+ *     dv_j = sum_{h in group} sum_r P_rj dO_r
+ * dq [Lq][H][D], dk and dv [Lk][Hkv][D] are overwritten.  Summed over the chunks of a ring (and
+ * over the slices, for dk/dv) they give the full backward.
+ */
+int orc_chunk_bwd(const double* q, int64_t Lq, const double* k, const double* v, int64_t Lk,
+                  int64_t q_offset, int64_t kv_offset, int causal, int H, int Hkv, int D,
+                  double scale, const double* out, const double* lse, const double* dout,
+                  double* dq, double* dk, double* dv, int nthreads) {
+    if (H <= 0 || Hkv <= 0 || D <= 0 || H % Hkv != 0 || Lq < 0 || Lk < 0) return ORC_BAD_ARG;
+    const int G = H / Hkv;
+    double* delta = (double*)malloc(sizeof(double) * (size_t)(Lq * H + 1));
+    if (delta == NULL) return ORC_NO_MEM;
+    set_threads(nthreads);
+    for (int64_t r = 0; r < Lq; ++r)
+        for (int h = 0; h < H; ++h) {
+            double dl = 0.0;
+            for (int d = 0; d < D; ++d)
+                dl += dout[(r * H + h) * (int64_t)D + d] * out[(r * H + h) * (int64_t)D + d];
+            delta[r * H + h] = dl;
+        }
+
+    /* dQ rows of the slice */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < Lq; ++r) {
+        for (int h = 0; h < H; ++h) {
+            const int g = h / G;
+            double* dqr = dq + (r * H + h) * (int64_t)D;
+            for (int d = 0; d < D; ++d) dqr[d] = 0.0;
+            const double* qr = q + (r * H + h) * (int64_t)D;
+            const double* dor = dout + (r * H + h) * (int64_t)D;
+            for (int64_t j = 0; j < Lk; ++j) {
+                if (causal && kv_offset + j > q_offset + r) continue;
+                const double* kj = k + (j * Hkv + g) * (int64_t)D;
+                const double* vj = v + (j * Hkv + g) * (int64_t)D;
+                double dot = 0.0, dp = 0.0;
+                for (int d = 0; d < D; ++d) { dot += qr[d] * kj[d]; dp += dor[d] * vj[d]; }
+                const double p = exp(scale * dot - lse[r * H + h]);
+                const double ds = p * (dp - delta[r * H + h]);
+                for (int d = 0; d < D; ++d) dqr[d] += scale * ds * kj[d];
+            }
+        }
+    }
+
+    /* dK and dV rows of the chunk */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t j = 0; j < Lk; ++j) {
+        for (int g = 0; g < Hkv; ++g) {
+            double* dkj = dk + (j * Hkv + g) * (int64_t)D;
+            double* dvj = dv + (j * Hkv + g) * (int64_t)D;
+            for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
+            const double* kj = k + (j * Hkv + g) * (int64_t)D;
+            const double* vj = v + (j * Hkv + g) * (int64_t)D;
+            for (int hh = 0; hh < G; ++hh) {
+                const int h = g * G + hh;
+                for (int64_t r = 0; r < Lq; ++r) {
+                    if (causal && kv_offset + j > q_offset + r) continue;
+                    const double* qr = q + (r * H + h) * (int64_t)D;
+                    const double* dor = dout + (r * H + h) * (int64_t)D;
+                    double dot = 0.0, dp = 0.0;
+                    for (int d = 0; d < D; ++d) { dot += qr[d] * kj[d]; dp += dor[d] * vj[d]; }
+                    const double p = exp(scale * dot - lse[r * H + h]);
+                    const double ds = p * (dp - delta[r * H + h]);
+                    for (int d = 0; d < D; ++d) {
+                        dkj[d] += scale * ds * qr[d];
+                        dvj[d] += p * dor[d];
+                    }
+                }
+            }
+        }
+    }
+    free(delta);
+    return ORC_OK;
+}
+
+/*
  * Log-sum-exp merge of two normalised partials over disjoint key sets (the ring's per-step
  * combination, Digest §3.2).  In place on (o_acc, lse_acc), n rows of H heads:
  *     m = max(l1, l2), w_k = exp(l_k - m), o = (w1 o1 + w2 o2) / (w1 + w2), l = m + ln(w1 + w2).

@@ -295,6 +295,72 @@ def test_backward_group_identities_and_row_selection():
     assert np.array_equal(dk2, dk[krows]) and np.array_equal(dv2, dv[krows])
 
 
+# ------------------------------------------------------- ring-chunk backward
+
+@pytest.mark.parametrize("cuts_q,cuts_k", [([0, 13], [0, 5, 13]), ([0, 6, 13], [0, 9, 13]),
+                                           ([0, 4, 9, 13], [0, 4, 9, 13])])
+def test_chunk_backward_over_a_ring_partition_sums_to_the_full_backward(cuts_q, cuts_k):
+    # One causal sequence of 13 tokens, its rows cut into slices and its keys into chunks.
+    # Given the full forward's out and lse, every slice x chunk step adds its share: dQ of a
+    # slice is the sum over chunks, dK/dV of a chunk the sum over slices (ring reading of the
+    # pages' long-sequence path; the reference is the separately written packed backward).
+    S, H, Hkv, D, scale = 13, 4, 2, 5, 0.6
+    q, k, v, do = rnd(80, S, H, D), rnd(81, S, Hkv, D), rnd(82, S, Hkv, D), rnd(83, S, H, D)
+    cu = np.array([0, S])
+    out, lse = oracle.varlen_fwd(q, k, v, cu, scale)
+    dq_ref, dk_ref, dv_ref = oracle.varlen_bwd(q, k, v, do, cu, scale)
+    dq = np.zeros_like(dq_ref)
+    dk = np.zeros_like(dk_ref)
+    dv = np.zeros_like(dv_ref)
+    for a, b in zip(cuts_q[:-1], cuts_q[1:]):
+        for c, e in zip(cuts_k[:-1], cuts_k[1:]):
+            gq, gk, gv = oracle.chunk_bwd(q[a:b], k[c:e], v[c:e], a, c, True, scale,
+                                          out[a:b], lse[a:b], do[a:b])
+            dq[a:b] += gq
+            dk[c:e] += gk
+            dv[c:e] += gv
+    np.testing.assert_allclose(dq, dq_ref, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_ref, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_ref, atol=1e-12)
+
+
+def test_future_chunk_backward_is_zero():
+    # A chunk entirely after the slice contributes nothing (every pair masked).
+    H, Hkv, D = 2, 1, 3
+    q, k, v, do = rnd(84, 4, H, D), rnd(85, 5, Hkv, D), rnd(86, 5, Hkv, D), rnd(87, 4, H, D)
+    out, lse = rnd(88, 4, H, D), rnd(89, 4, H)
+    dq, dk, dv = oracle.chunk_bwd(q, k, v, 10, 14, True, 0.5, out, lse, do)
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_non_causal_chunk_backward_matches_central_differences():
+    # Non-causal slice x chunk: L = sum(dO * out) with out from the oracle's chunk partial;
+    # the analytic gradients must match central differences of L.
+    Lq, Lk, H, Hkv, D, scale = 3, 4, 2, 1, 3, 0.8
+    q, k, v, do = rnd(90, Lq, H, D), rnd(91, Lk, Hkv, D), rnd(92, Lk, Hkv, D), rnd(93, Lq, H, D)
+
+    def L(qq, kk, vv):
+        o, _ = oracle.chunk_partial(qq, kk, vv, 7, 2, False, scale)
+        return float(np.sum(do * o))
+
+    out, lse = oracle.chunk_partial(q, k, v, 7, 2, False, scale)
+    dq, dk, dv = oracle.chunk_bwd(q, k, v, 7, 2, False, scale, out, lse, do)
+    eps = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args[name] = xp
+            lp = L(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = L(args["q"], args["k"], args["v"])
+            num[idx] = (lp - lm) / (2 * eps)
+        assert np.max(np.abs(num - g)) < 1e-7 * max(1.0, np.max(np.abs(num))), name
+
+
 # ----------------------------------------------------------------------- FLOPs
 
 
