@@ -121,11 +121,28 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
     fl = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D) for c in range(w.n_chunks))
     _, merge_ms = timed_launches(lambda: ops.hdp_lse_merge(acc_o, acc_l, po, pl), steps, warmup, torch)
     merge_bytes = w.q_len * w.H * (12 * w.D + 12)
+    # the share's backward: 16 chunk backward steps into fp32 accumulators, given the merged
+    # forward result (out rounded to bf16, lse) and a seeded dO
+    ring_step()
+    out_bf16 = acc_o.to(torch.bfloat16)
+    dout = synth.ring_bwd_tensors(w)[2].cuda()
+    dq_acc = torch.zeros_like(acc_o)
+    dk_acc = torch.zeros((L, w.Hkv, w.D), dtype=torch.float32, device="cuda")
+    dv_acc = torch.zeros_like(dk_acc)
+
+    def ring_bwd_step():
+        for c in range(w.n_chunks):
+            ops.hdp_attn_chunk_bwd(q, chunks[c][0], chunks[c][1], w.q_offset, c * L, out_bf16, acc_l,
+                                   dout, dq_acc, dk_acc, dv_acc, causal=True, scale=w.scale)
+
+    bms, _ = timed_launches(ring_bwd_step, rs, max(2, warmup // 10), torch)
+    fb = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D, 1) for c in range(w.n_chunks))
     out["ring_chunks_128k"] = {"ms_per_step": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
                                "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "merge_us": merge_ms * 1e3,
-                               "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9}
-    del q, k, v, chunks, acc_o, acc_l, po, pl
+                               "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
+                               "bwd_ms_per_step": bms, "bwd_TFLOP/s": fb / (bms * 1e-3) / 1e12}
+    del q, k, v, chunks, acc_o, acc_l, po, pl, out_bf16, dout, dq_acc, dk_acc, dv_acc
     # backward (and forward + backward) on the 8K slice and on one 8K sequence
     for make in (synth.fwd_bwd_8k_slice, synth.fwd_bwd_8k_single):
         w = make()

@@ -119,6 +119,26 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
                         float scale, void* dq, void* dk, void* dv, hipStream_t stream);
 
 /*
+ * Backward of one ring step (the counterpart of hdp_attn_chunk_partial): the slice's rows
+ * against one key/value chunk, at the same global offsets and with the same visibility.  With
+ * the slice's final output and lse (over all of its keys, e.g. the merged ring result) it adds
+ * this chunk's share of the gradients:
+ *     dq_acc += scale dS K,   dk_acc += scale dS^T Q,   dv_acc += P^T dO,
+ * P = exp(scale*S - lse) and dS = P * (dO V^T - rowsum(dO * out)) on the visible pairs, dK and
+ * dV summed over the H/Hkv query heads of each key/value head.  Summed over a ring's chunks
+ * (dq) and slices (dk, dv) this is the backward of the whole sequence (digest §3.2 ring steps).
+ *   q_slice, out, dout bf16 [Lq][H][D]; lse fp32 [Lq][H]; k_chunk, v_chunk bf16 [Lk][Hkv][D].
+ *   dq_acc fp32 [Lq][H][D]; dk_acc, dv_acc fp32 [Lk][Hkv][D]: read and updated in place
+ *   (zero them before the first step).  Offsets must be >= 0.  Uses a [2][H][Lq] fp32
+ *   workspace of the library.
+ */
+int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, const void* v_chunk,
+                       int32_t Lk, int64_t q_offset, int64_t kv_offset, int32_t causal,
+                       int32_t H, int32_t Hkv, int32_t D, float scale, const void* out,
+                       const float* lse, const void* dout, float* dq_acc, float* dk_acc,
+                       float* dv_acc, hipStream_t stream);
+
+/*
  * Exact attention FLOPs of one sequence of s tokens attending to itself: visible pairs
  * P = s(s+1)/2 (causal) or s^2, times H, times 4D (forward: score and value contractions),
  * 10D (backward: five contractions) or 14D (both).  The O(s^2) cost that drives data-aware

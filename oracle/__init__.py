@@ -58,7 +58,7 @@ def _load():
                                    P, i32]
     lib.orc_varlen_bwd.restype = i32
     lib.orc_chunk_bwd.argtypes = [P, i64, P, P, i64, i64, i64, i32, i32, i32, i32, f64, P, P, P, P,
-                                  P, P, i32]
+                                  i64, P, i64, P, P, P, i32]
     lib.orc_chunk_bwd.restype = i32
     lib.orc_count_pairs.argtypes = [i64, i64, i64, i64, i32]
     lib.orc_count_pairs.restype = ctypes.c_uint64
@@ -174,20 +174,28 @@ def varlen_bwd(q, k, v, dout, cu_seqlens, scale, qrows=None, krows=None, nthread
 
 
 def chunk_bwd(q_slice, k_chunk, v_chunk, q_offset, kv_offset, causal, scale, out, lse, dout,
-              nthreads=0):
+              qrows=None, krows=None, nthreads=0):
     """One ring step of the backward, given the slice's final out [Lq,H,D] and lse [Lq,H]:
-    returns this chunk's share (dq [Lq,H,D], dk [Lk,Hkv,D], dv [Lk,Hkv,D]) in fp64."""
+    returns this chunk's share (dq [nq,H,D], dk [nk,Hkv,D], dv [nk,Hkv,D]) in fp64, for the
+    selected slice rows / chunk rows (all by default)."""
     lib = _load()
     q, k, v = _f64(q_slice), _f64(k_chunk), _f64(v_chunk)
     o, l, do = _f64(out), _f64(lse), _f64(dout)
     Lq, H, D = q.shape
     Lk, Hkv = k.shape[0], k.shape[1]
-    dq = np.zeros((Lq, H, D), np.float64)
-    dk = np.zeros((Lk, Hkv, D), np.float64)
-    dv = np.zeros((Lk, Hkv, D), np.float64)
+    qr, n_q = _rows(qrows)
+    kr, n_k = _rows(krows)
+    if qr is None:
+        n_q = Lq
+    if kr is None:
+        n_k = Lk
+    dq = np.zeros((n_q, H, D), np.float64)
+    dk = np.zeros((n_k, Hkv, D), np.float64)
+    dv = np.zeros((n_k, Hkv, D), np.float64)
     st = lib.orc_chunk_bwd(_ptr(q), Lq, _ptr(k), _ptr(v), Lk, int(q_offset), int(kv_offset),
                            int(bool(causal)), H, Hkv, D, float(scale), _ptr(o), _ptr(l), _ptr(do),
-                           _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+                           _ptr(qr), n_q, _ptr(kr), n_k, _ptr(dq), _ptr(dk), _ptr(dv),
+                           int(nthreads))
     if st != ORC_OK:
         raise ValueError("orc_chunk_bwd failed with status %d" % st)
     return dq, dk, dv

@@ -213,12 +213,15 @@ int orc_chunk_partial(const double* q, int64_t Lq, const double* k, const double
  *     dq_r = scale sum_j P_rj (<dO_r, v_j> - delta_r) k_j          this chunk's share of dQ
  *     dk_j = scale sum_{h in group} sum_r P_rj (<dO_r, v_j> - delta_r) q_r
  *     dv_j = sum_{h in group} sum_r P_rj dO_r
- * dq [Lq][H][D], dk and dv [Lk][Hkv][D] are overwritten.  Summed over the chunks of a ring (and
- * over the slices, for dk/dv) they give the full backward.
+ * Summed over the chunks of a ring (and over the slices, for dk/dv) they give the full
+ * backward.  qrows / krows select the slice rows of dq and the chunk rows of dk, dv to evaluate
+ * (NULL = all); dq [n_q][H][D], dk and dv [n_k][Hkv][D] follow the order of the lists and are
+ * overwritten.
  */
 int orc_chunk_bwd(const double* q, int64_t Lq, const double* k, const double* v, int64_t Lk,
                   int64_t q_offset, int64_t kv_offset, int causal, int H, int Hkv, int D,
                   double scale, const double* out, const double* lse, const double* dout,
+                  const int64_t* qrows, int64_t n_q, const int64_t* krows, int64_t n_k,
                   double* dq, double* dk, double* dv, int nthreads) {
     if (H <= 0 || Hkv <= 0 || D <= 0 || H % Hkv != 0 || Lq < 0 || Lk < 0) return ORC_BAD_ARG;
     const int G = H / Hkv;
@@ -233,12 +236,16 @@ int orc_chunk_bwd(const double* q, int64_t Lq, const double* k, const double* v,
             delta[r * H + h] = dl;
         }
 
+    if (qrows == NULL) n_q = Lq;
+    if (krows == NULL) n_k = Lk;
+
     /* dQ rows of the slice */
 #pragma omp parallel for schedule(dynamic, 4)
-    for (int64_t r = 0; r < Lq; ++r) {
+    for (int64_t n = 0; n < n_q; ++n) {
+        const int64_t r = qrows ? qrows[n] : n;
         for (int h = 0; h < H; ++h) {
             const int g = h / G;
-            double* dqr = dq + (r * H + h) * (int64_t)D;
+            double* dqr = dq + (n * H + h) * (int64_t)D;
             for (int d = 0; d < D; ++d) dqr[d] = 0.0;
             const double* qr = q + (r * H + h) * (int64_t)D;
             const double* dor = dout + (r * H + h) * (int64_t)D;
@@ -257,10 +264,11 @@ int orc_chunk_bwd(const double* q, int64_t Lq, const double* k, const double* v,
 
     /* dK and dV rows of the chunk */
 #pragma omp parallel for schedule(dynamic, 4)
-    for (int64_t j = 0; j < Lk; ++j) {
+    for (int64_t n = 0; n < n_k; ++n) {
+        const int64_t j = krows ? krows[n] : n;
         for (int g = 0; g < Hkv; ++g) {
-            double* dkj = dk + (j * Hkv + g) * (int64_t)D;
-            double* dvj = dv + (j * Hkv + g) * (int64_t)D;
+            double* dkj = dk + (n * Hkv + g) * (int64_t)D;
+            double* dvj = dv + (n * Hkv + g) * (int64_t)D;
             for (int d = 0; d < D; ++d) { dkj[d] = 0.0; dvj[d] = 0.0; }
             const double* kj = k + (j * Hkv + g) * (int64_t)D;
             const double* vj = v + (j * Hkv + g) * (int64_t)D;

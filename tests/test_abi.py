@@ -139,5 +139,23 @@ def test_other_entry_points_validate_before_touching_the_gpu():
                                  0.1, FAKE, FAKE, FAKE, None) == _lib.HDP_ERR_INVALID_ARG
     assert L.hdp_attn_varlen_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 1, 10, 32, 8, 128,
                                  0.1, FAKE, FAKE, FAKE, None) == _lib.HDP_ERR_INVALID_ARG
+    # chunk backward: negative sizes/offsets, a null operand, bad heads, and empty work
+    cb = L.hdp_attn_chunk_bwd
+    assert cb(FAKE, -1, FAKE, FAKE, 8, 0, 0, 1, 32, 8, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+              FAKE, None) == _lib.HDP_ERR_INVALID_ARG
+    assert cb(FAKE, 8, FAKE, FAKE, 8, 0, -4, 1, 32, 8, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+              FAKE, None) == _lib.HDP_ERR_INVALID_ARG
+    assert cb(FAKE, 8, FAKE, FAKE, 8, 0, 0, 1, 32, 8, 128, 0.1, FAKE, FAKE, FAKE, NULL, FAKE,
+              FAKE, None) == _lib.HDP_ERR_INVALID_ARG
+    assert cb(FAKE, 8, FAKE, FAKE, 8, 0, 0, 1, 32, 8, 96, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+              FAKE, None) == _lib.HDP_ERR_UNSUPPORTED
+    assert cb(FAKE, 8, FAKE, FAKE, 8, 0, 0, 1, 30, 8, 128, 0.1, FAKE, FAKE, FAKE, FAKE, FAKE,
+              FAKE, None) == _lib.HDP_ERR_INVALID_ARG
+    assert cb(FAKE, 8, FAKE, FAKE, 8, 0, 0, 1, 32, 8, 128, float("nan"), FAKE, FAKE, FAKE, FAKE,
+              FAKE, FAKE, None) == _lib.HDP_ERR_INVALID_ARG
+    assert cb(NULL, 0, NULL, NULL, 8, 0, 0, 1, 32, 8, 128, 0.1, NULL, NULL, NULL, NULL, NULL,
+              NULL, None) == _lib.HDP_OK
+    assert cb(NULL, 8, NULL, NULL, 0, 0, 0, 1, 32, 8, 128, 0.1, NULL, NULL, NULL, NULL, NULL,
+              NULL, None) == _lib.HDP_OK
     for st in range(5):
         assert _lib.lib().hdp_status_string(st).startswith(b"HDP_")

@@ -333,6 +333,16 @@ def test_future_chunk_backward_is_zero():
     assert not dq.any() and not dk.any() and not dv.any()
 
 
+def test_chunk_backward_row_selection():
+    H, Hkv, D = 2, 1, 4
+    q, k, v, do = rnd(94, 20, H, D), rnd(95, 15, Hkv, D), rnd(96, 15, Hkv, D), rnd(97, 20, H, D)
+    out, lse = rnd(98, 20, H, D), rnd(99, 20, H)
+    a = oracle.chunk_bwd(q, k, v, 5, 3, True, 0.5, out, lse, do)
+    b = oracle.chunk_bwd(q, k, v, 5, 3, True, 0.5, out, lse, do, qrows=[3, 19, 0], krows=[14, 2])
+    assert np.array_equal(a[0][[3, 19, 0]], b[0])
+    assert np.array_equal(a[1][[14, 2]], b[1]) and np.array_equal(a[2][[14, 2]], b[2])
+
+
 def test_non_causal_chunk_backward_matches_central_differences():
     # Non-causal slice x chunk: L = sum(dO * out) with out from the oracle's chunk partial;
     # the analytic gradients must match central differences of L.

@@ -24,6 +24,8 @@ SIGNATURES = {
     "hdp_attn_chunk_partial": (I32, [P, I32, P, P, I32, I64, I64, I32, I32, I32, I32, F32, P, P, P]),
     "hdp_lse_merge": (I32, [P, P, P, P, I32, I32, I32, P, P]),
     "hdp_attn_varlen_bwd": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, P]),
+    "hdp_attn_chunk_bwd": (I32, [P, I32, P, P, I32, I64, I64, I32, I32, I32, I32, F32, P, P, P, P, P,
+                                 P, P]),
     "hdp_seq_flops": (U64, [I64, I32, I32, I32, I32]),
     "hdp_chunk_flops": (U64, [I32, I32, I64, I64, I32, I32, I32, I32]),
     "hdp_status_string": (ctypes.c_char_p, [I32]),

@@ -301,6 +301,55 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     return hdp::launch_bwd(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 
+int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, const void* v_chunk,
+                       int32_t Lk, int64_t q_offset, int64_t kv_offset, int32_t causal,
+                       int32_t H, int32_t Hkv, int32_t D, float scale, const void* out,
+                       const float* lse, const void* dout, float* dq_acc, float* dk_acc,
+                       float* dv_acc, hipStream_t stream) {
+    if (Lq < 0 || Lk < 0 || q_offset < 0 || kv_offset < 0) return HDP_ERR_INVALID_ARG;
+    if (int st = check_heads(H, Hkv, D)) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (q_offset > INT64_MAX / 4 || kv_offset > INT64_MAX / 4) return HDP_ERR_OVERFLOW;
+    if (Lq > (1 << 30) || Lk > (1 << 30)) return HDP_ERR_OVERFLOW;
+    if ((int64_t)Lq * H > (int64_t)INT32_MAX) return HDP_ERR_OVERFLOW;
+    if (Lq == 0 || Lk == 0) return HDP_OK;
+    if (!q_slice || !k_chunk || !v_chunk || !out || !lse || !dout || !dq_acc || !dk_acc || !dv_acc)
+        return HDP_ERR_INVALID_ARG;
+    DeviceState* st = nullptr;
+    if (int rc = device_state(&st)) return rc;
+    if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)Lq * (size_t)H)) return rc;
+    hdp::BwdArgs a{};
+    a.q = (const uint16_t*)q_slice;
+    a.k = (const uint16_t*)k_chunk;
+    a.v = (const uint16_t*)v_chunk;
+    a.out = (const uint16_t*)out;
+    a.lse = lse;
+    a.dout = (const uint16_t*)dout;
+    a.T = Lq;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.scale = scale;
+    a.scale_log2 = scale * kLog2e;
+    a.rowvals = (float*)st->ws;
+    a.Lq = Lq;
+    a.Lk = Lk;
+    // visibility depends only on q_offset - kv_offset clamped to [-Lq, Lk] (as in the forward)
+    const int64_t d = q_offset - kv_offset;
+    a.dpos = (int32_t)std::max<int64_t>(-(int64_t)Lq, std::min<int64_t>(d, Lk));
+    a.causal = causal ? 1 : 0;
+    a.dq_acc = dq_acc;
+    a.dk_acc = dk_acc;
+    a.dv_acc = dv_acc;
+    a.counters = st->counters;
+    a.hpw = heads_per_item(H, Hkv);
+    const int grid = st->cus;
+    const bool q8 = (H / a.hpw) % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
+    const bool kv8 = Hkv % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
+    a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
+    a.nqueues_kv = kv8 ? hdp::kMaxQueues : 1;
+    return hdp::launch_bwd_chunk(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
 int hdp_release_workspace(void) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return HDP_ERR_HIP;

@@ -97,7 +97,10 @@ __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // v
 // =============================================================================================
 // dQ kernel
 // =============================================================================================
-template <int D>
+// MODE 0: packed sequences (rows and keys of one sequence, causal); MODE 1: one ring step, the
+// slice's rows [Lq] against one chunk's keys [Lk] at a position offset, adding this chunk's
+// share of dQ to an fp32 accumulator.
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     using C = Cfg<D>;
     constexpr int kTile = kStage * C::kRowBytes;
@@ -116,9 +119,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     const int queue = blockIdx.x % args.nqueues_q;
     const int64_t q_stride = (int64_t)H * D, kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
+    const int Trv = MODE == 0 ? args.T : args.Lq;  // row stride of the lse2/delta planes
+    const bool causal = MODE == 0 ? true : (args.causal != 0);
+    const int dpos = MODE == 0 ? 0 : args.dpos;    // query position minus key position
 
     QueuePlan plan{0, 0, 0, 0};
-    if (wave == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane, args.T);
+    if (wave == 0) {
+        if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane, args.T);
+        else plan.total = ((args.Lq + W - 1) / W) * nhbq;
+    }
 
     for (;;) {
         if (wave == 0) {
@@ -126,8 +135,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
             if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
             k = __shfl(k, 0);
             int a = 0, len = 0, hbq = 0, c = 0;
-            const bool ok = k < plan.total &&
-                            queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
+            bool ok = k < plan.total;
+            if (ok) {
+                if (MODE == 0) {
+                    ok = queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
+                } else {
+                    len = args.Lq;
+                    hbq = k % nhbq;
+                    c = ((args.Lq + W - 1) / W) - k / nhbq;
+                }
+            }
             if (lane == 0) {
                 s_item[0] = ok ? a : -1;
                 s_item[1] = len;
@@ -138,8 +155,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         __syncthreads();
         const int a0 = __builtin_amdgcn_readfirstlane(s_item[0]);
         if (a0 < 0) break;
-        const int64_t base = a0;
+        const int64_t base = a0;                         // first row (and, packed, first key)
         const int s = __builtin_amdgcn_readfirstlane(s_item[1]);
+        const int sk = MODE == 0 ? s : args.Lk;          // keys
         const int hb = __builtin_amdgcn_readfirstlane(s_item[2]);
         const int tg = __builtin_amdgcn_readfirstlane(s_item[3]);
         const int head = hb * hpw + (wave % hpw);
@@ -148,7 +166,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         const int row = r_lo + l32;                      // this lane's query row
         const bool row_ok = row < s;
         const int wg_rmax = min(s, (tg + 1) * W) - 1;
-        const int n_units = wg_rmax / kUnit + 1;         // keys 0 .. wg_rmax
+        int jmax = sk - 1;                               // last key any row of the item sees
+        if (causal) jmax = min(jmax, wg_rmax + dpos);
+        const int n_units = jmax < 0 ? 0 : jmax / kUnit + 1;
         const int n_stages = (n_units + 1) / 2;
 
         // Q^T and dO^T fragments, delta = rowsum(dO * O), lse in log2 units
@@ -170,12 +190,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         }
         const float delta = xhalf_sum(dpart);
         const float lse2 = row_ok ? args.lse[(base + row) * H + head] * kLog2e : 0.f;
-        if (row_ok) args.rowvals[((int64_t)half * H + head) * args.T + base + row] = half == 0 ? lse2 : delta;
+        if (row_ok) args.rowvals[((int64_t)half * H + head) * Trv + base + row] = half == 0 ? lse2 : delta;
 
         f32x16 acc[C::kMT];
 #pragma unroll
         for (int mt = 0; mt < C::kMT; ++mt) acc[mt] = f32x16{};
 
+        const int64_t kbase = MODE == 0 ? base : 0;
         auto load_stage = [&](int st) {
             unsigned char* kb = smem[st % kStages][0];
             unsigned char* vb = smem[st % kStages][1];
@@ -183,15 +204,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
 #pragma unroll
             for (int i = 0; i < kBlocks / kWaves; ++i) {
                 const int blk = wave * (kBlocks / kWaves) + i;
-                dma_block<D>(args.k + (int64_t)g * D, kv_stride, base + st * kStage, s - 1 - st * kStage, blk, lane, kb);
-                dma_block<D>(args.v + (int64_t)g * D, kv_stride, base + st * kStage, s - 1 - st * kStage, blk, lane, vb);
+                dma_block<D>(args.k + (int64_t)g * D, kv_stride, kbase + st * kStage, sk - 1 - st * kStage, blk, lane, kb);
+                dma_block<D>(args.v + (int64_t)g * D, kv_stride, kbase + st * kStage, sk - 1 - st * kStage, blk, lane, vb);
             }
         };
-        load_stage(0);
-        if (n_stages > 1) load_stage(1);
+        if (n_units > 0) {
+            load_stage(0);
+            if (n_stages > 1) load_stage(1);
+        }
         wait_vm0();
         __syncthreads();
 
+        // key j of the item is visible to this lane's row iff j <= lim (and the row exists)
+        const int lim = causal ? min(row + dpos, sk - 1) : sk - 1;
         for (int u = 0; u < n_units; ++u) {
             if (u & 1) {
                 wait_vm0();
@@ -200,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
                 if (st < n_stages) load_stage(st);
             }
             const int j0 = u * kUnit;
-            if (j0 > r_lo + kUnit - 1) continue;             // every key after every row
+            if (causal && j0 > r_lo + kUnit - 1 + dpos) continue;   // every key after every row
             const unsigned char* kb = smem[(u >> 1) % kStages][0];
             const unsigned char* vb = smem[(u >> 1) % kStages][1];
             const int trow = (u & 1) * 32;
@@ -215,13 +240,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
                 dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[ks]),
                                                              __builtin_bit_cast(bf16x8, df[ks]), dP, 0, 0, 0);
             }
-            // key jl = 8*(i/4) + 4*half + (i%4) of the unit is visible iff j0 + jl <= row
-            const bool full = j0 + kUnit - 1 <= r_lo;
-            const int li = row - j0 - 4 * half;
+            // key jl = 8*(i/4) + 4*half + (i%4) of the unit is visible iff j0 + jl <= lim
+            const bool full = j0 + kUnit - 1 <= (causal ? min(r_lo + dpos, sk - 1) : sk - 1);
+            const int li = lim - j0 - 4 * half;
             bf16x8 ds[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const bool vis = full || (8 * (i >> 2) + (i & 3)) <= li;
+                const bool vis = row_ok && (full || (8 * (i >> 2) + (i & 3)) <= li);
                 const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -lse2)) : 0.f;
                 ds[i >> 3][i & 7] = (__bf16)(p * (dP[i] - delta));
             }
@@ -236,17 +261,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
 
         // dQ = scale * acc; lane holds d = mt*32 + 8*a4 + 4*half + (0..3) of its row
         if (row_ok) {
-            uint16_t* op = args.dq + ((base + row) * H + head) * D;
+            if (MODE == 0) {
+                uint16_t* op = args.dq + ((base + row) * H + head) * D;
 #pragma unroll
-            for (int mt = 0; mt < C::kMT; ++mt)
+                for (int mt = 0; mt < C::kMT; ++mt)
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const int d0 = mt * 32 + 8 * a4 + 4 * half;
-                    u32x2 w;
-                    w[0] = pack_bf16x2(acc[mt][4 * a4 + 0] * args.scale, acc[mt][4 * a4 + 1] * args.scale);
-                    w[1] = pack_bf16x2(acc[mt][4 * a4 + 2] * args.scale, acc[mt][4 * a4 + 3] * args.scale);
-                    *(u32x2*)(op + d0) = w;
-                }
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const int d0 = mt * 32 + 8 * a4 + 4 * half;
+                        u32x2 w;
+                        w[0] = pack_bf16x2(acc[mt][4 * a4 + 0] * args.scale, acc[mt][4 * a4 + 1] * args.scale);
+                        w[1] = pack_bf16x2(acc[mt][4 * a4 + 2] * args.scale, acc[mt][4 * a4 + 3] * args.scale);
+                        *(u32x2*)(op + d0) = w;
+                    }
+            } else if (n_units > 0) {
+                float* op = args.dq_acc + ((int64_t)row * H + head) * D;
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt)
+#pragma unroll
+                    for (int a4 = 0; a4 < 4; ++a4) {
+                        const int d0 = mt * 32 + 8 * a4 + 4 * half;
+                        f32x4 w = *(const f32x4*)(op + d0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) w[e] += acc[mt][4 * a4 + e] * args.scale;
+                        *(f32x4*)(op + d0) = w;
+                    }
+            }
         }
         __syncthreads();
     }
@@ -263,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
 // around the elementwise part of stage st (P = exp2(S c - lse2), dS = P (dP - delta)), one
 // element per slot.  Q and dO tiles (32 rows each) and the stage's 32 lse2 and delta values
 // arrive in LDS through direct global->LDS loads, in a ring of four stages two steps ahead.
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     using C = Cfg<D>;
     constexpr int kTile = kUnit * C::kRowBytes;           // 32 rows of Q or dO
@@ -289,7 +328,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     const int queue = blockIdx.x % args.nqueues_kv;
     const int64_t q_stride = (int64_t)H * D, kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
-    const int Trv = args.T;                                // row stride of the lse2/delta planes
+    const int Trv = MODE == 0 ? args.T : args.Lq;          // row stride of the lse2/delta planes
+    const bool causal = MODE == 0 ? true : (args.causal != 0);
+    const int dpos = MODE == 0 ? 0 : args.dpos;            // query position minus key position
 
     // per-lane LDS offsets: row fragments (A operand: row l32, slot (2ks+half)^swz), transposed
     // fragments (B operand over 16 rows x 32 columns, as the forward's V^T reads), stage loads
@@ -316,16 +357,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     }
 
     QueuePlan plan{0, 0, 0, 0};
-    if (wave == 0) plan = queue_plan(args.cu, args.n_seq, kKeyTile, nhbq, lane, args.T);
+    if (wave == 0) {
+        if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, kKeyTile, nhbq, lane, args.T);
+        else plan.total = ((args.Lk + kKeyTile - 1) / kKeyTile) * nhbq;
+    }
     auto publish = [&](int k, int slot) {
-        int a = 0, len = 0, hbq = 0, c = 0;
-        const bool ok = k < plan.total && queue_decode(args.cu, args.n_seq, plan, kKeyTile, nhbq, k, lane, a, len, hbq, c);
+        int a = 0, len = 0, hbq = 0, c = 0, kt = 0;
+        bool ok = k < plan.total;
+        if (ok) {
+            if (MODE == 0) {
+                ok = queue_decode(args.cu, args.n_seq, plan, kKeyTile, nhbq, k, lane, a, len, hbq, c);
+                // level c = tiles from this one to the end: earlier key tiles see more rows
+                kt = (len + kKeyTile - 1) / kKeyTile - c;
+            } else {
+                len = args.Lk;
+                hbq = k % nhbq;
+                kt = k / nhbq;                           // earlier key tiles see more rows
+            }
+        }
         if (lane == 0) {
             s_item[4 * slot + 0] = ok ? a : -1;
             s_item[4 * slot + 1] = len;
             s_item[4 * slot + 2] = queue + args.nqueues_kv * hbq;
-            // level c = tiles from this one to the end: earlier key tiles see more rows
-            s_item[4 * slot + 3] = (len + kKeyTile - 1) / kKeyTile - c;
+            s_item[4 * slot + 3] = kt;
         }
     };
     auto pop = [&]() {
@@ -342,23 +396,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         if (a0 < 0) break;
         int k_next = 0;
         if (wave == 0) k_next = pop();
-        const int64_t base = a0;
-        const int s = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
+        const int64_t base = a0;                        // packed: the sequence's first token
+        const int sk = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);   // keys
+        const int s = MODE == 0 ? sk : args.Lq;         // rows
         const int g = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 2]);
         const int kt = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 3]);
         const int kj0 = kt * kKeyTile + wave * kUnit;   // this wave's first key
         const int key = kj0 + l32;                      // this lane's key (B-operand column)
-        const int ru0 = kt * (kKeyTile / kUnit);
         const int n_ru = (s + kUnit - 1) / kUnit;
+        // first row unit with a row that sees a key of the tile
+        const int ru0 = causal ? max(0, kt * kKeyTile - dpos) / kUnit : 0;
         // stages (row unit, head), row units from the last one down to the key tile's diagonal:
         // the items of one key/value head start together at the sequence's end and move down
         // in step, so the workgroups of an XCD read the same Q/dO rows through its L2
-        const int n_st = (n_ru - ru0) * G;
+        const int n_st = max(0, n_ru - ru0) * G;
 
         // K^T and V^T fragments of this wave's 32 keys
         u32x4 kf[C::kKS], vf[C::kKS];
         {
-            const bool ok = key < s;
+            const bool ok = key < sk;
             const int64_t off = (base + key) * kv_stride + (int64_t)g * D + half * 8;
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks) {
@@ -436,12 +492,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         // invisible (key, row) pairs of stage st get S = -inf, so P = 0 and dS = 0
         auto stage_full = [&](int st) {
             const int r0 = (n_ru - 1 - st / G) * kUnit;
-            return kt * kKeyTile + kKeyTile - 1 <= r0 && r0 + kUnit <= s;
+            return (!causal || kt * kKeyTile + kKeyTile - 1 <= r0 + dpos) && r0 + kUnit <= s &&
+                   kt * kKeyTile + kKeyTile <= sk;
         };
         auto apply_mask = [&](int st, f32x16& S) {
             const int r0 = (n_ru - 1 - st / G) * kUnit;
             const int lim = min(s - 1 - r0, kUnit);     // rows r0 + jr with jr <= lim exist
-            const int kr = key - r0;                    // visible iff jr >= kr
+            // visible iff jr >= kr: the key exists and (causal) key <= row + dpos
+            const int kr = key >= sk ? kUnit : (causal ? max(key - dpos - r0, -1) : -1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int jr = 8 * (i >> 2) + 4 * half + (i & 3);
@@ -567,10 +625,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         }
 
         // dK = scale * dk, dV = dv; accumulator element i of D tile mt is key
-        // kj0 + 8*(i/4) + 4*half + (i%4), column mt*32 + l32.  Out through this wave's share of
-        // the ring (after every wave left the loop): rows of 32 keys, then 16-byte stores.
+        // kj0 + 8*(i/4) + 4*half + (i%4), column mt*32 + l32.
         __syncthreads();
-        {
+        if (MODE == 1) {
+            // add to the fp32 accumulators: 32 lanes cover 128 contiguous bytes of a key row
+            if (n_st > 0) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kr = kj0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if (kr < sk) {
+                        float* kp = args.dk_acc + ((int64_t)kr * Hkv + g) * D + l32;
+                        float* vp = args.dv_acc + ((int64_t)kr * Hkv + g) * D + l32;
+#pragma unroll
+                        for (int mt = 0; mt < C::kMT; ++mt) {
+                            kp[mt * 32] += dk[mt][i] * args.scale;
+                            vp[mt * 32] += dv[mt][i];
+                        }
+                    }
+                }
+            }
+        } else {
+            // out through this wave's share of the ring (after every wave left the loop): rows
+            // of 32 keys, then 16-byte stores
             unsigned char* tk = ring[wave].q;           // 32 keys x D bf16 each
             unsigned char* tv = ring[wave].d;
 #pragma unroll
@@ -591,7 +667,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
                 const int off = kr * C::kRowBytes + ((ch ^ swz(kr)) << 4);
                 const u32x4 wk = *(const u32x4*)(tk + off);
                 const u32x4 wv = *(const u32x4*)(tv + off);
-                if (kj0 + kr < s) {
+                if (kj0 + kr < sk) {
                     const int64_t o = ((base + kj0 + kr) * Hkv + g) * D + ch * 8;
                     *(u32x4*)(args.dk + o) = wk;
                     *(u32x4*)(args.dv + o) = wv;
@@ -608,11 +684,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
 
 hipError_t launch_bwd(const BwdArgs& a, int D, int grid, hipStream_t s) {
     if (D == 128) {
-        hipLaunchKernelGGL((bwd_dq_kernel<128>), dim3(grid), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, s, a);
     } else {
-        hipLaunchKernelGGL((bwd_dq_kernel<64>), dim3(grid), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_chunk(const BwdArgs& a, int D, int grid, hipStream_t s) {
+    if (D == 128) {
+        hipLaunchKernelGGL((bwd_dq_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_dq_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -69,9 +69,17 @@ struct BwdArgs {
     float scale_log2;
     float* rowvals;         // [2][H][T] workspace written by the dQ kernel: lse * log2(e) and
                             // delta = rowsum(dO * out), rows of one head contiguous
-    uint16_t* dq;
-    uint16_t* dk;
+    uint16_t* dq;           // varlen: bf16 [T][H][D]
+    uint16_t* dk;           // varlen: bf16 [T][Hkv][D]
     uint16_t* dv;
+    // chunk mode: q/out/dout/lse are the slice [Lq], k/v the chunk [Lk]; the results are added
+    // to fp32 accumulators (dq_acc [Lq][H][D], dk_acc / dv_acc [Lk][Hkv][D])
+    int32_t Lq, Lk;
+    int32_t dpos;           // q_offset - kv_offset clamped to [-Lq, Lk] (same visibility)
+    int32_t causal;
+    float* dq_acc;
+    float* dk_acc;
+    float* dv_acc;
     int* counters;
     int32_t hpw;            // query heads per dQ item
     int32_t nqueues_q;      // queues of the dQ kernel (8 or 1)
@@ -84,5 +92,6 @@ hipError_t launch_fwd_chunk(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int D, int grid, hipStream_t s);
+hipError_t launch_bwd_chunk(const BwdArgs& a, int D, int grid, hipStream_t s);
 
 }  // namespace hdp

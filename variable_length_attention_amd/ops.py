@@ -140,6 +140,29 @@ def hdp_attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None, dq=None
     return dq, dk, dv
 
 
+def hdp_attn_chunk_bwd(q_slice, k_chunk, v_chunk, q_offset: int, kv_offset: int, out, lse, dout,
+                       dq_acc, dk_acc, dv_acc, causal: bool = True, scale=None) -> None:
+    """One ring step of the backward: adds this chunk's share to the fp32 accumulators
+    dq_acc [Lq,H,D], dk_acc / dv_acc [Lk,Hkv,D] (in place)."""
+    for n, t in (("q_slice", q_slice), ("k_chunk", k_chunk), ("v_chunk", v_chunk), ("out", out),
+                 ("dout", dout)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("lse", lse, torch.float32, 2)
+    for n, t in (("dq_acc", dq_acc), ("dk_acc", dk_acc), ("dv_acc", dv_acc)):
+        _dev_tensor(n, t, torch.float32, 3)
+    Lq, H, D = q_slice.shape
+    Lk, Hkv = k_chunk.shape[0], k_chunk.shape[1]
+    if (tuple(out.shape) != (Lq, H, D) or tuple(dout.shape) != (Lq, H, D) or tuple(lse.shape) != (Lq, H)
+            or tuple(dq_acc.shape) != (Lq, H, D) or tuple(v_chunk.shape) != (Lk, Hkv, D)
+            or tuple(dk_acc.shape) != (Lk, Hkv, D) or tuple(dv_acc.shape) != (Lk, Hkv, D)):
+        raise ValueError("hdp_attn_chunk_bwd: inconsistent shapes")
+    st = _lib.lib().hdp_attn_chunk_bwd(_ptr(q_slice), Lq, _ptr(k_chunk), _ptr(v_chunk), Lk,
+                                       int(q_offset), int(kv_offset), int(bool(causal)), H, Hkv, D,
+                                       _scale(D, scale), _ptr(out), _ptr(lse), _ptr(dout),
+                                       _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _stream())
+    _lib.check("hdp_attn_chunk_bwd", st)
+
+
 def hdp_seq_flops(s: int, H: int, D: int, causal: bool = True, pass_: int = PASS_FWD) -> int:
     return int(_lib.lib().hdp_seq_flops(int(s), int(H), int(D), int(bool(causal)), int(pass_)))
 

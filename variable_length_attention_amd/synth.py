@@ -188,3 +188,18 @@ def ring_tensors(w: Workload, rng_seed: Optional[int] = None):
     k = normal(rng, (L, w.Hkv, w.D), w.dtype)
     v = normal(rng, (L, w.Hkv, w.D), w.dtype)
     return q, k, v
+
+
+def ring_bwd_tensors(w: Workload, seed: int = 5):
+    """Backward inputs of a ring share that do not come from any forward: out [q_len,H,D] and dO
+    [q_len,H,D] standard normal (bf16), and lse [q_len,H] = ln(number of keys the row sees over
+    the whole sequence) + 0.5, the lse of standard-normal scores at unit scale, so exp(x - lse)
+    stays near 1/count."""
+    import torch
+
+    rng = np.random.default_rng(seed + 1000)
+    out = normal(rng, (w.q_len, w.H, w.D), w.dtype)
+    dout = normal(rng, (w.q_len, w.H, w.D), w.dtype)
+    count = np.arange(w.q_len, dtype=np.float64) + w.q_offset + 1
+    lse = torch.from_numpy(np.repeat((np.log(count) + 0.5)[:, None], w.H, axis=1).astype(np.float32))
+    return out, lse, dout
