@@ -151,6 +151,16 @@ uint64_t hdp_seq_flops(int64_t s, int32_t H, int32_t D, int32_t causal, int32_t 
 uint64_t hdp_chunk_flops(int32_t Lq, int32_t Lk, int64_t q_offset, int64_t kv_offset,
                          int32_t causal, int32_t H, int32_t D, int32_t pass);
 
+/*
+ * Front/back chunk pairing of one sequence over a ring of n_ranks ranks (digest §4: each packed
+ * subsequence is cut into 2N chunks handed out in front/back pairs, which balances the causal
+ * mask).  Chunk c covers tokens [floor(c s / 2N), floor((c+1) s / 2N)); rank k holds chunks k
+ * and 2N-1-k.  Writes their global offsets and lengths to offsets[0..1], lengths[0..1] (front
+ * chunk first).  When 2N divides s every rank's causal pairs, summed over all chunks of the
+ * ring, are equal.  Host only.  s >= 0, 0 <= rank < n_ranks.
+ */
+int hdp_pair_chunks(int64_t s, int32_t n_ranks, int32_t rank, int64_t* offsets, int64_t* lengths);
+
 /* Static text for a status code. */
 const char* hdp_status_string(int status);
 

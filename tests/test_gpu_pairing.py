@@ -1,0 +1,82 @@
+"""GPU: one long causal sequence over a ring with front/back chunk pairing.
+
+Each rank holds query chunks k and 2N-1-k and sees every chunk of the ring once: its merged
+chunk partials must equal full causal attention for its rows (oracle), and the chunk backward
+summed over the whole ring must equal the oracle's packed backward.  Every rank is simulated on
+the one GPU in turn."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, grad_close, lse_close, max_abs
+from variable_length_attention_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def tensors(S, H, Hkv, D, seed):
+    rng = np.random.default_rng(seed)
+    return (synth.normal(rng, (S, H, D), "bf16"), synth.normal(rng, (S, Hkv, D), "bf16"),
+            synth.normal(rng, (S, Hkv, D), "bf16"), synth.normal(rng, (S, H, D), "bf16"))
+
+
+def rank_forward(q, k, v, S, N, rank, scale):
+    """Rank `rank`'s merged outputs for its two query chunks: [(offset, o, lse)]."""
+    chunks = [c for r in range(N) for c in ops.hdp_pair_chunks(S, N, r)]
+    res = []
+    for qo, ql in ops.hdp_pair_chunks(S, N, rank):
+        acc_o = acc_l = None
+        for ko, kl in chunks:
+            if ko > qo + ql - 1:
+                continue                               # a future chunk: nothing visible
+            o, l = ops.hdp_attn_chunk_partial(q[qo:qo + ql], k[ko:ko + kl], v[ko:ko + kl], qo, ko,
+                                              True, scale)
+            if acc_o is None:
+                acc_o, acc_l = o, l
+            else:
+                ops.hdp_lse_merge(acc_o, acc_l, o, l)
+        res.append((qo, acc_o, acc_l))
+    return res
+
+
+@pytest.mark.parametrize("S,N,H,Hkv,D", [(512, 4, 8, 2, 128), (600, 3, 4, 2, 64)])
+def test_paired_ring_forward_equals_full_attention(S, N, H, Hkv, D):
+    q, k, v, _ = tensors(S, H, Hkv, D, 120 + N)
+    scale = 1 / math.sqrt(D)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    ref_o, ref_l = oracle.varlen_fwd(q, k, v, np.array([0, S]), scale)
+    for rank in range(N):
+        for qo, o, l in rank_forward(qg, kg, vg, S, N, rank, scale):
+            torch.cuda.synchronize()
+            n = o.shape[0]
+            assert max_abs(o, ref_o[qo:qo + n]) <= TOL_BF16_OUT
+            lse_close(l, ref_l[qo:qo + n], TOL_BF16_LSE)
+
+
+def test_paired_ring_backward_sums_to_the_packed_backward():
+    S, N, H, Hkv, D = 512, 4, 8, 2, 128
+    q, k, v, do = tensors(S, H, Hkv, D, 130)
+    scale = 1 / math.sqrt(D)
+    cu = np.array([0, S], dtype=np.int32)
+    o, l = oracle.varlen_fwd(q, k, v, cu, scale)
+    out = torch.from_numpy(o).to(torch.bfloat16).cuda()
+    lse = torch.from_numpy(l).to(torch.float32).cuda()
+    qg, kg, vg, dog = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    dq = torch.zeros((S, H, D), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((S, Hkv, D), dtype=torch.float32, device="cuda")
+    dv = torch.zeros((S, Hkv, D), dtype=torch.float32, device="cuda")
+    chunks = [c for r in range(N) for c in ops.hdp_pair_chunks(S, N, r)]
+    for rank in range(N):
+        for qo, ql in ops.hdp_pair_chunks(S, N, rank):
+            for ko, kl in chunks:
+                ops.hdp_attn_chunk_bwd(qg[qo:qo + ql], kg[ko:ko + kl], vg[ko:ko + kl], qo, ko,
+                                       out[qo:qo + ql], lse[qo:qo + ql], dog[qo:qo + ql],
+                                       dq[qo:qo + ql], dk[ko:ko + kl], dv[ko:ko + kl],
+                                       causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, scale)
+    for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        grad_close(g, r)

@@ -28,6 +28,7 @@ SIGNATURES = {
                                  P, P]),
     "hdp_seq_flops": (U64, [I64, I32, I32, I32, I32]),
     "hdp_chunk_flops": (U64, [I32, I32, I64, I64, I32, I32, I32, I32]),
+    "hdp_pair_chunks": (I32, [I64, I32, I32, P, P]),
     "hdp_status_string": (ctypes.c_char_p, [I32]),
     "hdp_release_workspace": (I32, []),
 }

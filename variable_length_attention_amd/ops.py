@@ -5,6 +5,7 @@ in libhdpattn.so.  Outputs not supplied by the caller are allocated here with to
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional, Tuple
 
@@ -171,6 +172,16 @@ def hdp_chunk_flops(Lq: int, Lk: int, q_offset: int, kv_offset: int, causal: boo
                     D: int, pass_: int = PASS_FWD) -> int:
     return int(_lib.lib().hdp_chunk_flops(int(Lq), int(Lk), int(q_offset), int(kv_offset),
                                           int(bool(causal)), int(H), int(D), int(pass_)))
+
+
+def hdp_pair_chunks(s: int, n_ranks: int, rank: int):
+    """Front/back pairing: [(offset, length) of chunk rank, (offset, length) of chunk 2N-1-rank]."""
+    off = (ctypes.c_int64 * 2)()
+    ln = (ctypes.c_int64 * 2)()
+    st = _lib.lib().hdp_pair_chunks(int(s), int(n_ranks), int(rank), ctypes.addressof(off),
+                                    ctypes.addressof(ln))
+    _lib.check("hdp_pair_chunks", st)
+    return [(int(off[0]), int(ln[0])), (int(off[1]), int(ln[1]))]
 
 
 def hdp_release_workspace() -> None:
