@@ -143,6 +143,47 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
                                "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
                                "bwd_ms_per_step": bms, "bwd_TFLOP/s": fb / (bms * 1e-3) / 1e12}
     del q, k, v, chunks, acc_o, acc_l, po, pl, out_bf16, dout, dq_acc, dk_acc, dv_acc
+    # the same 128K sequence over the same 16 ranks with front/back chunk pairing: rank k holds
+    # query chunks k and 31-k (4096 tokens each) and meets all 32 chunks; every rank does the
+    # same causal work (rank 0 and rank 15 timed), against the contiguous share above
+    w = synth.ring_chunks_128k()
+    S = w.n_chunks * w.chunk_len
+    N = w.n_chunks
+    _, kfull, vfull = synth.ring_tensors(w)
+    kfull, vfull = kfull.cuda(), vfull.cuda()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.tensor_seed + 7)
+    qfull = torch.randn((S, w.H, w.D), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    allc = [c for r in range(N) for c in ops.hdp_pair_chunks(S, N, r)]
+    pair_rows = {}
+    for rank in (0, N - 1):
+        mine = ops.hdp_pair_chunks(S, N, rank)
+        bufs = [(torch.empty((ql, w.H, w.D), dtype=torch.float32, device="cuda"),
+                 torch.empty((ql, w.H), dtype=torch.float32, device="cuda"),
+                 torch.empty((ql, w.H, w.D), dtype=torch.float32, device="cuda"),
+                 torch.empty((ql, w.H), dtype=torch.float32, device="cuda")) for _, ql in mine]
+        steps_ = [(i, qo, ql, ko, kl) for i, (qo, ql) in enumerate(mine) for ko, kl in allc
+                  if ko <= qo + ql - 1]
+
+        def pair_step():
+            first = [True, True]
+            for i, qo, ql, ko, kl in steps_:
+                ao, al, po_, pl_ = bufs[i]
+                if first[i]:
+                    ops.hdp_attn_chunk_partial(qfull[qo:qo + ql], kfull[ko:ko + kl], vfull[ko:ko + kl],
+                                               qo, ko, True, w.scale, o_partial=ao, lse=al)
+                    first[i] = False
+                else:
+                    ops.hdp_attn_chunk_partial(qfull[qo:qo + ql], kfull[ko:ko + kl], vfull[ko:ko + kl],
+                                               qo, ko, True, w.scale, o_partial=po_, lse=pl_)
+                    ops.hdp_lse_merge(ao, al, po_, pl_)
+
+        pms, _ = timed_launches(pair_step, rs, max(2, warmup // 10), torch)
+        pfl = sum(ops.hdp_chunk_flops(ql, kl, qo, ko, True, w.H, w.D) for _, qo, ql, ko, kl in steps_)
+        pair_rows["rank%d" % rank] = {"ms_per_step": pms, "GFLOP": pfl / 1e9,
+                                      "TFLOP/s": pfl / (pms * 1e-3) / 1e12, "calls": len(steps_)}
+    out["ring_pairs_128k"] = pair_rows
+    del kfull, vfull, qfull
     # backward (and forward + backward) on the 8K slice and on one 8K sequence
     for make in (synth.fwd_bwd_8k_slice, synth.fwd_bwd_8k_single):
         w = make()
