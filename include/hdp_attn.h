@@ -161,6 +161,46 @@ uint64_t hdp_chunk_flops(int32_t Lq, int32_t Lk, int64_t q_offset, int64_t kv_of
  */
 int hdp_pair_chunks(int64_t s, int32_t n_ranks, int32_t rank, int64_t* offsets, int64_t* lengths);
 
+/*
+ * HDP sharding of one global batch over a pool of ranks of capacity C tokens (digest §3.1 and
+ * Figure 2), host only.  A sequence longer than C gets a ring of ceil(s/C) units (one unit per
+ * rank: near-equal contiguous slices, or with pair != 0 the front/back chunk pairs of
+ * hdp_pair_chunks); shorter sequences are packed by best fit (decreasing length) into units of
+ * at most C tokens.  Units list the rings by decreasing length, then the packed units.
+ *   lens [n_seq] (>= 0; zero-length sequences are dropped).  Outputs (caller-owned):
+ *   unit_first_piece [n_units + 1] (pieces of unit j are unit_first_piece[j] ..
+ *   unit_first_piece[j+1] - 1), unit_ring [n_units] (the sequence index of a ring unit, -1 for
+ *   a packed unit), piece_seq / piece_off / piece_len [n_pieces] (sequence, first token within
+ *   it, token count).  *n_units and *n_pieces always receive the sizes needed; if they exceed
+ *   max_units or max_pieces nothing else is written and HDP_ERR_OVERFLOW is returned.
+ */
+int hdp_plan_shard(const int64_t* lens, int32_t n_seq, int64_t C, int32_t pair, int32_t max_units,
+                   int32_t max_pieces, int32_t* n_units, int32_t* n_pieces, int32_t* unit_first_piece,
+                   int32_t* unit_ring, int32_t* piece_seq, int64_t* piece_off, int64_t* piece_len);
+
+/*
+ * Attention FLOPs of every unit of a plan from hdp_plan_shard (pass as in hdp_seq_flops): a
+ * packed unit costs the hdp_seq_flops of its sequences; a ring unit its query pieces against
+ * every piece of its ring (hdp_chunk_flops, causal).  cost [n_units] (written).  Host only.
+ */
+int hdp_plan_unit_flops(const int64_t* lens, int32_t n_seq, int32_t n_units,
+                        const int32_t* unit_first_piece, const int32_t* unit_ring,
+                        const int32_t* piece_seq, const int64_t* piece_off, const int64_t* piece_len,
+                        int32_t H, int32_t D, int32_t pass, uint64_t* cost);
+
+/*
+ * Balance scheduler, DP-Balance (digest §3.4, Figure 4), host only: assigns units of equal
+ * tokens but unequal cost to n_ranks ranks so that their summed costs meet; ranks may run
+ * different numbers of units.  Items are packed units and whole rings (the consecutive units
+ * of one ring run on distinct ranks), sorted by per-rank cost and cut into n_ranks buckets of
+ * about equal FLOPs; every rank that trails the most loaded one by more than delta (all ranks
+ * when none does) takes, least loaded first, the next item of the first non-empty bucket.
+ *   cost, unit_ring [n_units] as from hdp_plan_unit_flops / hdp_plan_shard.  Outputs:
+ *   unit_rank [n_units], rank_load [n_ranks].  A ring wider than the pool is invalid.
+ */
+int hdp_plan_balance(const uint64_t* cost, const int32_t* unit_ring, int32_t n_units,
+                     int32_t n_ranks, uint64_t delta, int32_t* unit_rank, uint64_t* rank_load);
+
 /* Static text for a status code. */
 const char* hdp_status_string(int status);
 

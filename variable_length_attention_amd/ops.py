@@ -184,5 +184,76 @@ def hdp_pair_chunks(s: int, n_ranks: int, rank: int):
     return [(int(off[0]), int(ln[0])), (int(off[1]), int(ln[1]))]
 
 
+class Plan:
+    """A plan from hdp_plan_shard: per unit, its ring (sequence index, -1 if packed) and its
+    pieces [(sequence, offset, length)]; the flat arrays are kept for the other planner calls."""
+
+    def __init__(self, lens, first, ring, pseq, poff, plen):
+        self.lens, self.first, self.ring = lens, first, ring
+        self.pseq, self.poff, self.plen = pseq, poff, plen
+
+    def __len__(self):
+        return len(self.ring)
+
+    def units(self):
+        return [(int(self.ring[j]), [(int(self.pseq[p]), int(self.poff[p]), int(self.plen[p]))
+                                     for p in range(self.first[j], self.first[j + 1])])
+                for j in range(len(self.ring))]
+
+
+def _i64(xs):
+    return (ctypes.c_int64 * max(1, len(xs)))(*[int(x) for x in xs])
+
+
+def hdp_plan_shard(lens, C: int, pair: bool = False) -> Plan:
+    L = _lib.lib()
+    n = len(lens)
+    lens_c = _i64(lens)
+    nu, npc = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = L.hdp_plan_shard(ctypes.addressof(lens_c), n, int(C), int(bool(pair)), 0, 0,
+                          ctypes.addressof(nu), ctypes.addressof(npc), None, None, None, None, None)
+    if st not in (_lib.HDP_OK, _lib.HDP_ERR_OVERFLOW):
+        _lib.check("hdp_plan_shard", st)
+    U, Pn = nu.value, npc.value
+    first = (ctypes.c_int32 * (U + 1))()
+    ring = (ctypes.c_int32 * max(1, U))()
+    pseq = (ctypes.c_int32 * max(1, Pn))()
+    poff = (ctypes.c_int64 * max(1, Pn))()
+    plen = (ctypes.c_int64 * max(1, Pn))()
+    st = L.hdp_plan_shard(ctypes.addressof(lens_c), n, int(C), int(bool(pair)), U, Pn,
+                          ctypes.addressof(nu), ctypes.addressof(npc), ctypes.addressof(first),
+                          ctypes.addressof(ring), ctypes.addressof(pseq), ctypes.addressof(poff),
+                          ctypes.addressof(plen))
+    _lib.check("hdp_plan_shard", st)
+    return Plan(lens_c, list(first), list(ring)[:U], pseq, poff, plen)
+
+
+def hdp_plan_unit_flops(plan: Plan, H: int, D: int, pass_: int = PASS_FWD):
+    U = len(plan)
+    first = (ctypes.c_int32 * (U + 1))(*plan.first)
+    ring = (ctypes.c_int32 * max(1, U))(*plan.ring)
+    cost = (ctypes.c_uint64 * max(1, U))()
+    st = _lib.lib().hdp_plan_unit_flops(ctypes.addressof(plan.lens), len(plan.lens) if U else 0, U,
+                                        ctypes.addressof(first), ctypes.addressof(ring),
+                                        ctypes.addressof(plan.pseq), ctypes.addressof(plan.poff),
+                                        ctypes.addressof(plan.plen), int(H), int(D), int(pass_),
+                                        ctypes.addressof(cost))
+    _lib.check("hdp_plan_unit_flops", st)
+    return [int(c) for c in cost][:U]
+
+
+def hdp_plan_balance(cost, unit_ring, n_ranks: int, delta: int = 0):
+    """Returns (rank of each unit, load of each rank)."""
+    U = len(cost)
+    c = (ctypes.c_uint64 * max(1, U))(*[int(x) for x in cost])
+    r = (ctypes.c_int32 * max(1, U))(*[int(x) for x in unit_ring])
+    ur = (ctypes.c_int32 * max(1, U))()
+    load = (ctypes.c_uint64 * n_ranks)()
+    st = _lib.lib().hdp_plan_balance(ctypes.addressof(c), ctypes.addressof(r), U, int(n_ranks),
+                                     int(delta), ctypes.addressof(ur), ctypes.addressof(load))
+    _lib.check("hdp_plan_balance", st)
+    return [int(x) for x in ur][:U], [int(x) for x in load]
+
+
 def hdp_release_workspace() -> None:
     _lib.check("hdp_release_workspace", _lib.lib().hdp_release_workspace())
