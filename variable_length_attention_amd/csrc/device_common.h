@@ -107,6 +107,8 @@ struct QueuePlan {
     int Tc;      // clamped token count
     int nt0;     // tile count of sequence `lane` (0 past n_seq): the first 64 sequences stay in
                  // registers, so decoding touches memory only for sequences 64 and up
+    int st0;     // start and length of sequence `lane` (clamped)
+    int ln0;
 };
 
 __device__ inline int seq_tiles(const int32_t* cu, int i, int Tc, int W) {
@@ -127,7 +129,10 @@ __device__ inline QueuePlan queue_plan(const int32_t* cu, int n_seq, int W, int 
                                        int Tbound = 0x7fffffff) {
     QueuePlan p;
     p.Tc = min(max(cu[n_seq], 0), Tbound);
-    p.nt0 = lane < n_seq ? seq_tiles(cu, lane, p.Tc, W) : 0;
+    p.st0 = 0;
+    p.ln0 = 0;
+    if (lane < n_seq) seq_span(cu, lane, p.Tc, p.st0, p.ln0);
+    p.nt0 = (p.ln0 + W - 1) / W;
     int sum = p.nt0, mx = p.nt0;
     for (int i = lane + 64; i < n_seq; i += 64) {
         const int nt = seq_tiles(cu, i, p.Tc, W);
@@ -170,7 +175,12 @@ __device__ inline bool queue_decode(const int32_t* cu, int n_seq, const QueuePla
         }
     }
     if (seq < 0) return false;
-    seq_span(cu, seq, p.Tc, a, len);
+    if (seq < 64) {
+        a = __builtin_amdgcn_readlane(p.st0, seq);
+        len = __builtin_amdgcn_readlane(p.ln0, seq);
+    } else {
+        seq_span(cu, seq, p.Tc, a, len);
+    }
     return true;
 }
 
