@@ -100,12 +100,20 @@ __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // v
 // MODE 0: packed sequences (rows and keys of one sequence, causal); MODE 1: one ring step, the
 // slice's rows [Lq] against one chunk's keys [Lk] at a position offset, adding this chunk's
 // share of dQ to an fp32 accumulator.
+//
+// Software-pipelined like the forward, over units of 32 keys: step u issues the dQ product of
+// unit u-1 (8 MFMAs) and the S and dP products of unit u+1 (16 MFMAs) around the elementwise
+// part of unit u (P = exp2(S c - lse2), dS = P (dP - delta), one element per slot).  K and V
+// arrive through direct global->LDS loads in a ring of three 64-key stages; K and V rows are
+// read for the products of unit u+1 at the start of a step, the transposed K fragments of
+// unit u once the dQ product of unit u-1 has been issued.
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     using C = Cfg<D>;
     constexpr int kTile = kStage * C::kRowBytes;
+    constexpr int kBPW = kStage / C::kRowsPerBlock / kWaves;   // 1 KB stage loads per wave and tile
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][kTile];
-    __shared__ int s_item[4];
+    __shared__ int s_item[8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,43 +131,73 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     const bool causal = MODE == 0 ? true : (args.causal != 0);
     const int dpos = MODE == 0 ? 0 : args.dpos;    // query position minus key position
 
+    // per-lane LDS offsets: row fragments (A operand: row l32 of a 32-row unit, slot
+    // (2 ks + half) ^ swz), transposed fragments (as the forward's V^T reads), stage loads
+    int rofs[4];
+    {
+        const int t = half ^ swz(l32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rofs[j] = l32 * C::kRowBytes + 16 * ((2 * j) ^ t);
+    }
+    int tofs[2];
+    {
+        const int gidx = lane >> 4;
+        const int tr_row = 4 * (gidx >> 1) + ((lane & 15) >> 2);
+        const int tr_col = 16 * (gidx & 1) + 4 * (lane & 3);
+        const int t = (tr_col >> 3) ^ swz(tr_row);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) tofs[j] = tr_row * C::kRowBytes + 16 * ((4 * j) ^ t) + (lane & 1) * 8;
+    }
+    int grow[kBPW], gchunk[kBPW];
+#pragma unroll
+    for (int i = 0; i < kBPW; ++i) {
+        grow[i] = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
+        gchunk[i] = (lane % C::kChunks) ^ swz(grow[i]);
+    }
+
     QueuePlan plan{0, 0, 0, 0, 0, 0};
     if (wave == 0) {
         if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane, args.T);
         else plan.total = ((args.Lq + W - 1) / W) * nhbq;
     }
-
-    for (;;) {
-        if (wave == 0) {
-            int k = 0;
-            if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
-            k = __shfl(k, 0);
-            int a = 0, len = 0, hbq = 0, c = 0;
-            bool ok = k < plan.total;
-            if (ok) {
-                if (MODE == 0) {
-                    ok = queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
-                } else {
-                    len = args.Lq;
-                    hbq = k % nhbq;
-                    c = ((args.Lq + W - 1) / W) - k / nhbq;
-                }
-            }
-            if (lane == 0) {
-                s_item[0] = ok ? a : -1;
-                s_item[1] = len;
-                s_item[2] = queue + args.nqueues_q * hbq;
-                s_item[3] = c - 1;
+    auto publish = [&](int k, int slot) {
+        int a = 0, len = 0, hbq = 0, c = 0;
+        bool ok = k < plan.total;
+        if (ok) {
+            if (MODE == 0) {
+                ok = queue_decode(args.cu, args.n_seq, plan, W, nhbq, k, lane, a, len, hbq, c);
+            } else {
+                len = args.Lq;
+                hbq = k % nhbq;
+                c = ((args.Lq + W - 1) / W) - k / nhbq;
             }
         }
-        __syncthreads();
-        const int a0 = __builtin_amdgcn_readfirstlane(s_item[0]);
+        if (lane == 0) {
+            s_item[4 * slot + 0] = ok ? a : -1;
+            s_item[4 * slot + 1] = len;
+            s_item[4 * slot + 2] = queue + args.nqueues_q * hbq;
+            s_item[4 * slot + 3] = c - 1;
+        }
+    };
+    auto pop = [&]() {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
+        return k;
+    };
+    if (wave == 0) publish(__shfl(pop(), 0), 0);
+    __syncthreads();
+
+    for (int it = 0;; ++it) {
+        const int slot = it & 1;
+        const int a0 = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
         if (a0 < 0) break;
+        int k_next = 0;
+        if (wave == 0) k_next = pop();
         const int64_t base = a0;                         // first row (and, packed, first key)
-        const int s = __builtin_amdgcn_readfirstlane(s_item[1]);
+        const int s = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
         const int sk = MODE == 0 ? s : args.Lk;          // keys
-        const int hb = __builtin_amdgcn_readfirstlane(s_item[2]);
-        const int tg = __builtin_amdgcn_readfirstlane(s_item[3]);
+        const int hb = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 2]);
+        const int tg = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 3]);
         const int head = hb * hpw + (wave % hpw);
         const int g = (hb * hpw) / G;
         const int r_lo = tg * W + (wave / hpw) * kUnit;
@@ -170,6 +208,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         if (causal) jmax = min(jmax, wg_rmax + dpos);
         const int n_units = jmax < 0 ? 0 : jmax / kUnit + 1;
         const int n_stages = (n_units + 1) / 2;
+        const int64_t kbase = MODE == 0 ? base : 0;
+
+        // stage st (64 keys, clamped into the key range) into ring buffer st % 3
+        auto load_stage = [&](int st) {
+            unsigned char* kb = smem[st % kStages][0];
+            unsigned char* vb = smem[st % kStages][1];
+#pragma unroll
+            for (int i = 0; i < kBPW; ++i) {
+                const int blk = wave * kBPW + i;
+                const int64_t off = (kbase + min(st * kStage + grow[i], sk - 1)) * kv_stride + (int64_t)g * D + gchunk[i] * 8;
+                __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+            }
+        };
+        if (n_units > 0) {
+            load_stage(0);
+            if (n_stages > 1) load_stage(1);
+        }
 
         // Q^T and dO^T fragments, delta = rowsum(dO * O), lse in log2 units
         u32x4 qf[C::kKS], df[C::kKS];
@@ -191,72 +247,144 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         const float delta = xhalf_sum(dpart);
         const float lse2 = row_ok ? args.lse[(base + row) * H + head] * kLog2e : 0.f;
         if (row_ok) args.rowvals[((int64_t)half * H + head) * Trv + base + row] = half == 0 ? lse2 : delta;
+        wait_vm0();
+        __syncthreads();
+
+        auto unit_base = [&](int u, int kv) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)(lds_addr(smem[(u >> 1) % kStages][kv]) + (u & 1) * 32 * C::kRowBytes));
+        };
+        auto read_rows = [&](int u, int kv, u32x4 (&f)[C::kKS]) {
+            const uint32_t b = unit_base(u, kv);
+            uint32_t a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = lds_add(b, rofs[j]);
+#pragma unroll
+            for (int ks = 0; ks < C::kKS; ++ks) f[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
+        };
+        auto read_cols = [&](int u, int kv, bf16x8 (&f)[2][C::kMT]) {
+            const uint32_t b = unit_base(u, kv);
+            const uint32_t a[2] = {lds_add(b, tofs[0]), lds_add(b, tofs[1])};
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt) {
+                    const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
+                    f[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
+                    f[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
+                }
+        };
+        // key j of the item is visible to this lane's row iff j <= lim (and the row exists);
+        // invisible elements of a unit get S = -inf, so P = 0 and dS = 0
+        const int lim = row_ok ? (causal ? min(row + dpos, sk - 1) : sk - 1) : -1;
+        auto unit_full = [&](int u) {
+            const int j0 = u * kUnit;
+            return j0 + kUnit - 1 <= (causal ? min(r_lo + dpos, sk - 1) : sk - 1) && r_lo + kUnit <= s;
+        };
+        auto apply_mask = [&](int u, f32x16& S) {
+            const int li = max(-1, min(lim - u * kUnit, kUnit)) - 4 * half;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S[i] = (8 * (i >> 2) + (i & 3)) > li ? -INFINITY : S[i];
+        };
+        auto stage_turn = [&](int u) {
+            wait_vm0();
+            __syncthreads();
+            const int st = (u + 3) >> 1;
+            if (st < n_stages) load_stage(st);
+        };
 
         f32x16 acc[C::kMT];
 #pragma unroll
         for (int mt = 0; mt < C::kMT; ++mt) acc[mt] = f32x16{};
+        bf16x8 kt[2][C::kMT];                           // K^T fragments of the previous unit
 
-        const int64_t kbase = MODE == 0 ? base : 0;
-        auto load_stage = [&](int st) {
-            unsigned char* kb = smem[st % kStages][0];
-            unsigned char* vb = smem[st % kStages][1];
-            constexpr int kBlocks = kStage / C::kRowsPerBlock;      // per tile
-#pragma unroll
-            for (int i = 0; i < kBlocks / kWaves; ++i) {
-                const int blk = wave * (kBlocks / kWaves) + i;
-                dma_block<D>(args.k + (int64_t)g * D, kv_stride, kbase + st * kStage, sk - 1 - st * kStage, blk, lane, kb);
-                dma_block<D>(args.v + (int64_t)g * D, kv_stride, kbase + st * kStage, sk - 1 - st * kStage, blk, lane, vb);
-            }
-        };
-        if (n_units > 0) {
-            load_stage(0);
-            if (n_stages > 1) load_stage(1);
-        }
-        wait_vm0();
-        __syncthreads();
-
-        // key j of the item is visible to this lane's row iff j <= lim (and the row exists)
-        const int lim = causal ? min(row + dpos, sk - 1) : sk - 1;
-        for (int u = 0; u < n_units; ++u) {
-            if (u & 1) {
-                wait_vm0();
-                __syncthreads();
-                const int st = (u + 3) >> 1;
-                if (st < n_stages) load_stage(st);
-            }
-            const int j0 = u * kUnit;
-            if (causal && j0 > r_lo + kUnit - 1 + dpos) continue;   // every key after every row
-            const unsigned char* kb = smem[(u >> 1) % kStages][0];
-            const unsigned char* vb = smem[(u >> 1) % kStages][1];
-            const int trow = (u & 1) * 32;
+        // step u: dQ of u-1 (operands Tp, kt), S/dP of u+1 into Sn/Dn, elementwise of u from
+        // Sc/Dc into Tc
+        auto step = [&](int u, bool odd, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn,
+                        const bf16x8 (&Tp)[2], bf16x8 (&Tc)[2]) {
+            if (odd) stage_turn(u);
             u32x4 kf[C::kKS], vf[C::kKS];
-            lds_rows_frag<D>(kb, trow + l32, half, kf);
-            lds_rows_frag<D>(vb, trow + l32, half, vf);
-            f32x16 S = f32x16{}, dP = f32x16{};
+            const int un = min(u + 1, n_units - 1);      // past the end: harmless re-read
+            read_rows(un, 0, kf);
+            read_rows(un, 1, vf);
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int kDQ = 2 * C::kMT;              // dQ MFMAs
+            constexpr int kSD = 2 * C::kKS;              // S and dP MFMAs
+            constexpr int kSlots = kDQ + kSD > 16 ? kDQ + kSD : 16;
+            uint32_t tw[8];
+            float te = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < C::kKS; ++ks) {
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]),
-                                                            __builtin_bit_cast(bf16x8, qf[ks]), S, 0, 0, 0);
-                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[ks]),
-                                                             __builtin_bit_cast(bf16x8, df[ks]), dP, 0, 0, 0);
+            for (int k = 0; k < kSlots; ++k) {
+                if (k == kDQ) {
+                    read_cols(u, 0, kt);                 // K^T of unit u, for the next step
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (k < kDQ) {
+                    const int ks2 = k / C::kMT, mt = k % C::kMT;
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks2][mt], Tp[ks2], acc[mt], 0, 0, 0);
+                } else if (k < kDQ + kSD) {
+                    const int j = k - kDQ, ks = j >> 1;
+                    if (j == 0) Sn = f32x16{};
+                    if (j == 1) Dn = f32x16{};
+                    if ((j & 1) == 0) Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[ks]), Sn, 0, 0, 0);
+                    else Dn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[ks]), __builtin_bit_cast(bf16x8, df[ks]), Dn, 0, 0, 0);
+                }
+                if (k < 16) {
+                    const int i = k;
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[i], c2, -lse2));
+                    const float t = p * (Dc[i] - delta);
+                    if (i & 1) {
+                        tw[i >> 1] = pack_bf16x2(te, t);
+                        asm volatile("" : "+v"(tw[i >> 1]));
+                    } else {
+                        te = t;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // key jl = 8*(i/4) + 4*half + (i%4) of the unit is visible iff j0 + jl <= lim
-            const bool full = j0 + kUnit - 1 <= (causal ? min(r_lo + dpos, sk - 1) : sk - 1);
-            const int li = lim - j0 - 4 * half;
-            bf16x8 ds[2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const bool vis = row_ok && (full || (8 * (i >> 2) + (i & 3)) <= li);
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(S[i], c2, -lse2)) : 0.f;
-                ds[i >> 3][i & 7] = (__bf16)(p * (dP[i] - delta));
+            for (int h = 0; h < 2; ++h)
+                Tc[h] = __builtin_bit_cast(bf16x8, u32x4{tw[4 * h], tw[4 * h + 1], tw[4 * h + 2], tw[4 * h + 3]});
+            if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
+        };
+
+        if (n_units > 0) {
+            f32x16 SA, DA, SB, DB;
+            bf16x8 TA[2], TB[2];
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                for (int mt = 0; mt < C::kMT; ++mt) kt[ks2][mt] = bf16x8{};
+            TA[0] = bf16x8{};
+            TA[1] = bf16x8{};
+            {
+                u32x4 kf[C::kKS], vf[C::kKS];
+                read_rows(0, 0, kf);
+                read_rows(0, 1, vf);
+                SA = f32x16{};
+                DA = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < C::kKS; ++ks) {
+                    SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[ks]), SA, 0, 0, 0);
+                    DA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vf[ks]), __builtin_bit_cast(bf16x8, df[ks]), DA, 0, 0, 0);
+                }
             }
-            bf16x8 kt[2][C::kMT];
-            lds_cols_frag<D>(kb, trow, lane, kt);
+            if (!unit_full(0)) apply_mask(0, SA);
+            int u = 0;
+            for (; u + 1 < n_units; u += 2) {
+                step(u, false, SA, DA, SB, DB, TA, TB);
+                step(u + 1, true, SB, DB, SA, DA, TB, TA);
+            }
+            const bf16x8 (&TL)[2] = (u < n_units) ? TB : TA;
+            if (u < n_units) step(u, false, SA, DA, SB, DB, TA, TB);
+            // the dQ product of the last unit (its K^T was read in its step)
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
                 for (int mt = 0; mt < C::kMT; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks2][mt], ds[ks2], acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks2][mt], TL[ks2], acc[mt], 0, 0, 0);
         }
 
         // dQ = scale * acc; lane holds d = mt*32 + 8*a4 + 4*half + (0..3) of its row
@@ -287,6 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
                     }
             }
         }
+        if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();
     }
     if (tid == 0) queue_finish(args.counters);
