@@ -53,6 +53,20 @@ def test_backward_small_packs_full(lengths, H, Hkv, D):
               % (lengths, H, Hkv, D, name, *e))
 
 
+def test_backward_more_than_64_sequences_full():
+    # long sequences at index 64 and later: their spans come from memory in the work queue
+    rng = np.random.default_rng(42)
+    lengths = [int(x) for x in rng.integers(0, 70, size=130)]
+    lengths[64], lengths[90], lengths[129] = 400, 260, 150
+    lengths[5] = lengths[66] = 0
+    w, q, k, v, do, cu = case(lengths, 8, 2, 128, seed=43)
+    dq, dk, dv = run_fwd_bwd(w, q, k, v, do, cu)
+    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, w.scale)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        e = grad_close(g, r)
+        print("%d sequences %s: max %.3g, beyond half-ulp %.3g, mean %.2g" % (len(lengths), name, *e))
+
+
 def test_backward_is_deterministic_and_isolated_per_sequence():
     lengths = [150, 64, 257]
     w, q, k, v, do, cu = case(lengths, 32, 8, 128, seed=41)

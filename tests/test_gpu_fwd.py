@@ -110,6 +110,29 @@ def test_sequence_permutation_permutes_rows_bitwise():
     assert torch.equal(lse0[ig].view(torch.int32), lse1.view(torch.int32))
 
 
+def many_lengths(n=150, seed=21):
+    """n ragged sequences (empty ones included) with long ones at index 64 (the first sequence
+    whose span the work queue reads from memory rather than from registers) and later on."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(x) for x in rng.integers(0, 90, size=n)]
+    lengths[64] = 700
+    lengths[100] = 450
+    lengths[n - 1] = 333
+    for i in (3, 70, 120):
+        lengths[i] = 0
+    return lengths
+
+
+def test_more_than_64_sequences_full():
+    lengths = many_lengths()
+    w, q, k, v, cu = varlen_case(lengths, 8, 2, 128, seed=22)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print("%d sequences, %d tokens: max|dout|=%.3g max|dlse|=%.3g" % (len(lengths), int(cu[-1]), e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+
+
 def test_every_row_is_written_and_runs_are_deterministic():
     w, q, k, v, cu = varlen_case([5, 700, 64, 0, 129], 32, 8, 128, seed=14)
     qg, kg, vg = to_gpu(q, k, v)
