@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         gchunk[i] = (lane % C::kChunks) ^ swz(grow[i]);
     }
 
-    QueuePlan plan{0, 0, 0, 0, 0, 0};
+    QueuePlan plan{0, 0, 0, 0, 0, 0, 0, 0};
     if (wave == 0) {
         if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane, args.T);
         else plan.total = ((args.Lq + W - 1) / W) * nhbq;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         gchunk[i] = (lane % C::kChunks) ^ swz(grow[i]);
     }
 
-    QueuePlan plan{0, 0, 0, 0, 0, 0};
+    QueuePlan plan{0, 0, 0, 0, 0, 0, 0, 0};
     if (wave == 0) {
         if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, kKeyTile, nhbq, lane, args.T);
         else plan.total = ((args.Lk + kKeyTile - 1) / kKeyTile) * nhbq;

@@ -109,6 +109,8 @@ struct QueuePlan {
                  // registers, so decoding touches memory only for sequences 64 and up
     int st0;     // start and length of sequence `lane` (clamped)
     int ln0;
+    int la;      // with at most 64 sequences and 64 levels (fast): items above level lane + 1,
+    int fast;    // per head block, so decoding is a wave vote instead of a search
 };
 
 __device__ inline int seq_tiles(const int32_t* cu, int i, int Tc, int W) {
@@ -141,6 +143,11 @@ __device__ inline QueuePlan queue_plan(const int32_t* cu, int n_seq, int W, int 
     }
     p.total = wave_sum(sum) * nhbq;
     p.maxc = wave_max(mx);
+    p.la = 0;
+    p.fast = n_seq <= 64 && p.maxc <= 64;
+    if (p.fast) {
+        for (int i = 0; i < n_seq; ++i) p.la += max(0, __builtin_amdgcn_readlane(p.nt0, i) - (lane + 1));
+    }
     return p;
 }
 
@@ -148,14 +155,23 @@ __device__ inline QueuePlan queue_plan(const int32_t* cu, int n_seq, int W, int 
 // Returns false only if the plan does not match cu_seqlens (never for k < total).
 __device__ inline bool queue_decode(const int32_t* cu, int n_seq, const QueuePlan& p, int W, int nhbq,
                                     int k, int lane, int& a, int& len, int& hbq, int& c) {
-    int lo = 1, hi = p.maxc;   // smallest level with levels_above(level) * nhbq <= k
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (levels_above(cu, n_seq, p, W, mid, lane) * nhbq <= k) hi = mid;
-        else lo = mid + 1;
+    int j;
+    if (p.fast) {
+        // levels_above falls with the level: the smallest level c with levels_above(c) * nhbq
+        // <= k is the lowest lane that votes yes (lane c - 1 holds level c)
+        const uint64_t m = __ballot(lane < p.maxc && p.la * nhbq <= k);
+        c = (int)__builtin_ctzll(m) + 1;
+        j = k - __builtin_amdgcn_readlane(p.la, c - 1) * nhbq;
+    } else {
+        int lo = 1, hi = p.maxc;   // smallest level with levels_above(level) * nhbq <= k
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (levels_above(cu, n_seq, p, W, mid, lane) * nhbq <= k) hi = mid;
+            else lo = mid + 1;
+        }
+        c = lo;
+        j = k - levels_above(cu, n_seq, p, W, c, lane) * nhbq;
     }
-    c = lo;
-    const int j = k - levels_above(cu, n_seq, p, W, c, lane) * nhbq;
     int r = j / nhbq;
     hbq = j % nhbq;
     int seq = -1;

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     const float c2 = args.scale_log2;
 
     // ---- per-launch queue plan (wave 0 only) ----
-    QueuePlan plan{0, 0, 0, 0};
+    QueuePlan plan{0, 0, 0, 0, 0, 0, 0, 0};
     if (wave == 0) {
         if (MODE == 0) plan = queue_plan(args.cu, args.n_seq, W, nhbq, lane);
         else plan.total = ((args.Lq + W - 1) / W) * nhbq;
