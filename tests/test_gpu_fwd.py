@@ -133,6 +133,21 @@ def test_more_than_64_sequences_full():
     assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
 
 
+@pytest.mark.parametrize("lengths", [[4096, 17, 0, 300], [4097, 5, 64]])
+def test_work_queue_level_boundary_sampled(lengths):
+    # with 4 query heads per key/value head an item spans 64 rows: a 4096-token sequence has 64
+    # tile levels (the last that the per-lane level table holds), 4097 tokens have 65
+    w, q, k, v, cu = varlen_case(lengths, 8, 2, 128, seed=23)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    rows = sample_rows(cu, 7)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    e_out, e_lse = max_abs(out[idx], ro), max_abs(lse[idx], rl)
+    print("lengths=%s: %d sampled rows, max|dout|=%.3g max|dlse|=%.3g" % (lengths, len(rows), e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
 def test_every_row_is_written_and_runs_are_deterministic():
     w, q, k, v, cu = varlen_case([5, 700, 64, 0, 129], 32, 8, 128, seed=14)
     qg, kg, vg = to_gpu(q, k, v)
