@@ -437,7 +437,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     constexpr int kTile = kUnit * C::kRowBytes;           // 32 rows of Q or dO
     constexpr int kBlocks = kUnit / C::kRowsPerBlock;      // 1 KB loads per tile
     constexpr int kBPW = kBlocks / kWaves;                 // per wave
-    constexpr int kRing = 4;
+    // Ring of eight 32-row stages, synchronised every other step.  Step s loads stage s+4 into
+    // the buffer of stage s-4, whose last reads (step s-4) every wave has finished by the
+    // barrier of the even step b = s or s-1.  Steps b and b+1 read the rows of stages b+1 and
+    // b+2 and the columns of stages b and b+1, so the barrier of step b first waits for every
+    // load but those of step b-1 (stage b+3).
+    constexpr int kRing = 8;
+    constexpr int kAhead = 4;
     constexpr int kLoadsPerStage = 2 * kBPW + 1;          // vector memory ops per stage, per wave
     struct Stage {
         unsigned char q[kTile];
@@ -641,10 +647,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         for (int mt = 0; mt < C::kMT; ++mt) { dk[mt] = f32x16{}; dv[mt] = f32x16{}; }
 
         if (n_st > 0) {
-            // prologue: stages 0..2 in flight, stage 0 scored
-            load_stage(0);
-            if (n_st > 1) load_stage(1);
-            if (n_st > 2) load_stage(2);
+            // prologue: stages 0 .. kAhead-1 loaded, stage 0 scored
+#pragma unroll
+            for (int p = 0; p < kAhead; ++p)
+                if (p < n_st) load_stage(p);
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
             f32x16 SA, DA, SB, DB;
@@ -666,16 +672,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
 
             // step st: dV/dK of st-1 (operands Pp, Tp, dt, qt), S/dP of st+1 into Sn/Dn, the
             // elementwise part of st from Sc/Dc into Pc/Tc
-            auto step = [&](int st, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn, const bf16x8 (&Pp)[2],
-                            const bf16x8 (&Tp)[2], bf16x8 (&Pc)[2], bf16x8 (&Tc)[2]) {
-                // stage st+1 must have landed; stage st+2 (issued one step ago) may still fly
-                if (st > 0) {
-                    if (st + 2 < n_st) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerStage);
+            auto step = [&](int st, bool even, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn,
+                            const bf16x8 (&Pp)[2], const bf16x8 (&Tp)[2], bf16x8 (&Pc)[2], bf16x8 (&Tc)[2]) {
+                __builtin_amdgcn_sched_barrier(0);          // steps stay apart in the schedule
+                if (even && st > 0) {
+                    if (st - 1 + kAhead < n_st) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerStage);
                     else __builtin_amdgcn_s_waitcnt(0x0F70);
                     __syncthreads();
                 }
-                // ring buffer of stage st+3 last held stage st-1, read up to step st-1
-                if (st + 3 < n_st) load_stage(st + 3);
+                if (st + kAhead < n_st) load_stage(st + kAhead);
                 u32x4 qr[C::kKS], dr[C::kKS];
                 const int sn = min(st + 1, n_st - 1);     // past the end: harmless re-read
                 constexpr int kH = C::kKS / 2;             // second half read mid-way
@@ -737,13 +742,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
             };
             int st = 0;
             for (; st + 1 < n_st; st += 2) {
-                step(st, SA, DA, SB, DB, PA, TA, PB, TB);
-                step(st + 1, SB, DB, SA, DA, PB, TB, PA, TA);
+                step(st, true, SA, DA, SB, DB, PA, TA, PB, TB);
+                step(st + 1, false, SB, DB, SA, DA, PB, TB, PA, TA);
             }
             // the dV/dK products of the last stage (its dt/qt were read in its step)
             const bf16x8 (&PL)[2] = (st < n_st) ? PB : PA;
             const bf16x8 (&TL)[2] = (st < n_st) ? TB : TA;
-            if (st < n_st) step(st, SA, DA, SB, DB, PA, TA, PB, TB);
+            if (st < n_st) step(st, true, SA, DA, SB, DB, PA, TA, PB, TB);
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
