@@ -437,13 +437,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     constexpr int kTile = kUnit * C::kRowBytes;           // 32 rows of Q or dO
     constexpr int kBlocks = kUnit / C::kRowsPerBlock;      // 1 KB loads per tile
     constexpr int kBPW = kBlocks / kWaves;                 // per wave
-    // Ring of eight 32-row stages, synchronised every other step.  Step s loads stage s+4 into
-    // the buffer of stage s-4, whose last reads (step s-4) every wave has finished by the
-    // barrier of the even step b = s or s-1.  Steps b and b+1 read the rows of stages b+1 and
-    // b+2 and the columns of stages b and b+1, so the barrier of step b first waits for every
-    // load but those of step b-1 (stage b+3).
+    // Ring of eight 32-row stages, synchronised every third step.  Step s loads stage s+5 into
+    // the buffer of stage s-3, whose last reads (step s-3) every wave has finished by the
+    // barrier of the step b = s, s-1 or s-2 that is a multiple of 3.  Steps b .. b+2 read the
+    // rows of stages b+1 .. b+3 and the columns of stages b .. b+2, so the barrier of step b
+    // first waits for every load but those of step b-1 (stage b+4).
     constexpr int kRing = 8;
-    constexpr int kAhead = 4;
+    constexpr int kAhead = 5;
+    constexpr int kSyncEvery = 3;
     constexpr int kLoadsPerStage = 2 * kBPW + 1;          // vector memory ops per stage, per wave
     struct Stage {
         unsigned char q[kTile];
@@ -672,10 +673,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
 
             // step st: dV/dK of st-1 (operands Pp, Tp, dt, qt), S/dP of st+1 into Sn/Dn, the
             // elementwise part of st from Sc/Dc into Pc/Tc
-            auto step = [&](int st, bool even, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn,
+            auto step = [&](int st, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn,
                             const bf16x8 (&Pp)[2], const bf16x8 (&Tp)[2], bf16x8 (&Pc)[2], bf16x8 (&Tc)[2]) {
                 __builtin_amdgcn_sched_barrier(0);          // steps stay apart in the schedule
-                if (even && st > 0) {
+                if (st > 0 && st % kSyncEvery == 0) {
                     if (st - 1 + kAhead < n_st) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerStage);
                     else __builtin_amdgcn_s_waitcnt(0x0F70);
                     __syncthreads();
@@ -742,13 +743,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
             };
             int st = 0;
             for (; st + 1 < n_st; st += 2) {
-                step(st, true, SA, DA, SB, DB, PA, TA, PB, TB);
-                step(st + 1, false, SB, DB, SA, DA, PB, TB, PA, TA);
+                step(st, SA, DA, SB, DB, PA, TA, PB, TB);
+                step(st + 1, SB, DB, SA, DA, PB, TB, PA, TA);
             }
             // the dV/dK products of the last stage (its dt/qt were read in its step)
             const bf16x8 (&PL)[2] = (st < n_st) ? PB : PA;
             const bf16x8 (&TL)[2] = (st < n_st) ? TB : TA;
-            if (st < n_st) step(st, true, SA, DA, SB, DB, PA, TA, PB, TB);
+            if (st < n_st) step(st, SA, DA, SB, DB, PA, TA, PB, TB);
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
