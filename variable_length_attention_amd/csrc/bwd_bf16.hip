@@ -89,7 +89,7 @@ __device__ inline void dma_block(const uint16_t* src, int64_t stride, int64_t ba
     const int slot = lane % Cfg<D>::kChunks;
     const int chunk = slot ^ swz(row);
     const int64_t r = base_row + min(row, last_row);
-    __builtin_amdgcn_global_load_lds(src + r * stride + chunk * 8, (lds_void*)(tile + blk * 1024), 16, 0, 0);
+    lds_dma16(src + r * stride + chunk * 8, lds_addr(tile + blk * 1024));
 }
 
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
@@ -218,8 +218,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
             for (int i = 0; i < kBPW; ++i) {
                 const int blk = wave * kBPW + i;
                 const int64_t off = (kbase + min(st * kStage + grow[i], sk - 1)) * kv_stride + (int64_t)g * D + gchunk[i] * 8;
-                __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+                lds_dma16(args.k + off, lds_addr(kb + blk * 1024));
+                lds_dma16(args.v + off, lds_addr(vb + blk * 1024));
             }
         };
         if (n_units > 0) {
@@ -570,13 +570,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
             for (int i = 0; i < kBPW; ++i) {
                 const int blk = wave * kBPW + i;
                 const int64_t off = (base + min(r0 + grow[i], s - 1)) * q_stride + (int64_t)head * D + gchunk[i] * 8;
-                __builtin_amdgcn_global_load_lds(args.q + off, (lds_void*)(S.q + blk * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(args.dout + off, (lds_void*)(S.d + blk * 1024), 16, 0, 0);
+                lds_dma16(args.q + off, lds_addr(S.q + blk * 1024));
+                lds_dma16(args.dout + off, lds_addr(S.d + blk * 1024));
             }
             {   // every wave loads the same 256 bytes, so all count the same memory ops
                 const int64_t r = base + min(r0 + l32, s - 1);
                 const float* src = args.rowvals + ((int64_t)half * H + head) * Trv + r;
-                __builtin_amdgcn_global_load_lds(src, (lds_void*)&S.rv[0][0], 4, 0, 0);
+                lds_dma4(src, lds_addr(&S.rv[0][0]));
             }
         };
         auto tile_base = [&](int st, int which) {   // uniform LDS address of a stage's tile

@@ -32,6 +32,37 @@ __device__ inline uint32_t lds_add(uint32_t base, uint32_t off) {
     return r;
 }
 
+// Direct global->LDS loads (the CDNA LDS DMA): every lane reads 16 (or 4) bytes at its own
+// global address and the wave writes them to LDS at lds + 16 * lane (or 4 * lane), without
+// passing through registers.  lds is wave-uniform and goes to M0, which is saved and restored
+// around the load.  The loads are issued from inline assembly on purpose: the compiler cannot
+// tell which LDS bytes a DMA writes, so for the builtin it waits for every outstanding global
+// load before the next LDS read of any buffer, which exposes the full memory latency once per
+// stage.  Callers order the loads against LDS reads themselves: s_waitcnt vmcnt and a workgroup
+// barrier before any wave reads a buffer that a load wrote.
+__device__ inline void lds_dma16(const void* g, uint32_t lds) {
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved) : "v"(g), "s"(lds) : "memory");
+}
+__device__ inline void lds_dma4(const void* g, uint32_t lds) {
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved) : "v"(g), "s"(lds) : "memory");
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;
 

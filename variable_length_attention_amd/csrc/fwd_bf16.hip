@@ -224,8 +224,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 for (int i = 0; i < C::kBlocksPerWave; ++i) {
                     const int blk = wave * C::kBlocksPerWave + i;
                     const int64_t off = (kbase + j0) * kv_stride + (int64_t)g * D + gofs[i];
-                    __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+                    lds_dma16(args.k + off, lds_addr(kb + blk * 1024));
+                    lds_dma16(args.v + off, lds_addr(vb + blk * 1024));
                 }
             } else {
 #pragma unroll
@@ -235,8 +235,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     const int chunk = (lane % C::kChunks) ^ swz(row);
                     const int j = min(j0 + row, sk - 1);
                     const int64_t off = (kbase + j) * kv_stride + (int64_t)g * D + chunk * 8;
-                    __builtin_amdgcn_global_load_lds(args.k + off, (lds_void*)(kb + blk * 1024), 16, 0, 0);
-                    __builtin_amdgcn_global_load_lds(args.v + off, (lds_void*)(vb + blk * 1024), 16, 0, 0);
+                    lds_dma16(args.k + off, lds_addr(kb + blk * 1024));
+                    lds_dma16(args.v + off, lds_addr(vb + blk * 1024));
                 }
             }
         };
