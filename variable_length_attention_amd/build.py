@@ -20,6 +20,10 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                 # MFMA accumulators in VGPRs: the online-softmax rescale touches the output
                 # accumulator with VALU ops, and AGPR accumulators would be copied every step.
                 "-mllvm", "-amdgpu-mfma-vgpr-form",
+                # Work-queue pops are single-lane atomics whose result is needed only at the end
+                # of an item; the atomic optimizer would rewrite them into a form that waits for
+                # the result right after the atomic.
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
                 "-I", INCLUDE, "-I", CSRC]
 
 

@@ -192,7 +192,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         const int a0 = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
         if (a0 < 0) break;
         int k_next = 0;
-        if (wave == 0) k_next = pop();
         const int64_t base = a0;                         // first row (and, packed, first key)
         const int s = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
         const int sk = MODE == 0 ? s : args.Lk;          // keys
@@ -387,6 +386,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
                     acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[ks2][mt], TL[ks2], acc[mt], 0, 0, 0);
         }
 
+        // the next item is taken when this workgroup is about to be free (taking it earlier
+        // would hand out large items before it is known which workgroup finishes first)
+        if (wave == 0) k_next = pop();
         // dQ = scale * acc; lane holds d = mt*32 + 8*a4 + 4*half + (0..3) of its row
         if (row_ok) {
             if (MODE == 0) {
@@ -531,7 +533,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         const int a0 = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
         if (a0 < 0) break;
         int k_next = 0;
-        if (wave == 0) k_next = pop();
         const int64_t base = a0;                        // packed: the sequence's first token
         const int sk = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);   // keys
         const int s = MODE == 0 ? sk : args.Lq;         // rows
@@ -759,6 +760,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
                 }
         }
 
+        // the next item is taken when this workgroup is about to be free (taking it earlier
+        // would hand out large items before it is known which workgroup finishes first)
+        if (wave == 0) k_next = pop();
         // dK = scale * dk, dV = dv; accumulator element i of D tile mt is key
         // kj0 + 8*(i/4) + 4*half + (i%4), column mt*32 + l32.
         __syncthreads();

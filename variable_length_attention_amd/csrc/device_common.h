@@ -102,6 +102,28 @@ __device__ inline int wave_max(int x) {
     return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
                max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
+// Stores through a raw buffer resource that covers `bytes` from `base`: a lane whose offset
+// lies outside is dropped by the hardware, so every lane of a wave issues the same store
+// instructions whatever rows exist.  That keeps the count of the wave's outstanding vector
+// memory operations fixed, so a later wait for an older operation (the queue pop) can leave
+// the stores in flight.  base and bytes are the same in every lane; reading them from the
+// first lane tells the compiler so.
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    // 0x00020000: 32-bit data format, the raw (untyped) buffer setting of this GPU family
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
+}
+__device__ inline void buf_store_b128(void* base, uint32_t bytes, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, uniform_rsrc(base, bytes), off, 0, 0);
+}
+__device__ inline void buf_store_b32(void* base, uint32_t bytes, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), uniform_rsrc(base, bytes), off, 0, 0);
+}
+constexpr uint32_t kDropOffset = 0x40000000u;   // beyond every resource the kernels build
+
 // Two floats to two bf16 (round to nearest even) in one dword, first in the low half.
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -171,7 +171,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // item fields are uniform: keep them in scalar registers
         const int it_a = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
         if (it_a < 0) break;
-        if (wave == 0) k_next = pop();
         const int64_t qbase = it_a;
         const int64_t kbase = MODE == 0 ? qbase : 0;
         const int s_rows = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
@@ -185,7 +184,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         const int head = hb * hpw + (wave % hpw);
         const int g = (hb * hpw) / G;
         const int r_lo = tg * W + (wave / hpw) * kRowsPerWave;   // this wave's first row
-        const bool wave_rows = r_lo < s_rows;
         // keys the workgroup visits
         const int wg_rmax = min(s_rows, (tg + 1) * W) - 1;
         int jmax = sk - 1;
@@ -361,7 +359,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // with 16-byte stores that fill complete cache lines.  A tile is 32 rows x 256 bytes (the
         // output row, or half of it for fp32 at D = 128), slots XOR-swizzled by the row.
         auto store_rows = [&](const f32x16 (&oo)[C::kMT][kNT], const float (&mm)[kNT], const float (&ll)[kNT]) {
-            if (!wave_rows) return;
             constexpr int kE = MODE == 0 ? 2 : 4;                  // output element bytes
             constexpr int kOutRow = D * kE;
             constexpr int kWb = kOutRow < kStageRowBytes ? kOutRow : kStageRowBytes;
@@ -376,7 +373,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 const float mb = (mm[nt] == -INFINITY) ? 0.f : mm[nt];
                 const float lse = lt > 0.f ? (mb + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
                 const int row0 = r_lo + nt * 32;                   // first row of this tile
-                if (half == 0 && row0 + l32 < s_rows) args.lse[(qbase + row0 + l32) * (int64_t)H + head] = lse;
+                // rows row0 .. row0 + nrows - 1 of this tile exist (none past the sequence's end)
+                const int nrows = max(0, min(32, s_rows - row0));
+                buf_store_b32(args.lse + (qbase + row0) * (int64_t)H + head, nrows > 0 ? (uint32_t)((nrows - 1) * H * 4 + 4) : 0u,
+                              half == 0 ? (uint32_t)(l32 * H * 4) : kDropOffset, lse);
 #pragma unroll
                 for (int b = 0; b < kNB; ++b) {
                     // fragment -> tile: lane (row l32, half) holds d = mt*32 + 8*a4 + 4*half + 0..3
@@ -400,15 +400,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                         }
                     }
                     // tile -> global: lane i covers slot i % kSlots of tile row i / kSlots (+ step)
+                    // (all reads first, so that their latencies overlap)
+                    constexpr int kReads = 32 / kRowsPerRead;
+                    u32x4 vals[kReads];
 #pragma unroll
-                    for (int rr = 0; rr < 32; rr += kRowsPerRead) {
-                        const int tr = rr + lane / kSlots, slot = lane % kSlots;
-                        const u32x4 val = *(const u32x4*)(tile + tr * kWb + ((slot ^ (tr % kSlots)) << 4));
-                        if (row0 + tr < s_rows) {
-                            unsigned char* gp = (unsigned char*)args.out +
-                                                ((qbase + row0 + tr) * (int64_t)H + head) * kOutRow + b * kWb + slot * 16;
-                            *(u32x4*)gp = val;
-                        }
+                    for (int i = 0; i < kReads; ++i) {
+                        const int tr = i * kRowsPerRead + lane / kSlots, slot = lane % kSlots;
+                        vals[i] = *(const u32x4*)(tile + tr * kWb + ((slot ^ (tr % kSlots)) << 4));
+                    }
+                    unsigned char* gb = (unsigned char*)args.out + ((qbase + row0) * (int64_t)H + head) * kOutRow + b * kWb;
+                    const uint32_t bytes = nrows > 0 ? (uint32_t)((nrows - 1) * H * kOutRow + kWb) : 0u;
+#pragma unroll
+                    for (int i = 0; i < kReads; ++i) {
+                        const int tr = i * kRowsPerRead + lane / kSlots, slot = lane % kSlots;
+                        buf_store_b128(gb, bytes, (uint32_t)(tr * H * kOutRow + slot * 16), vals[i]);
                     }
                 }
             }
@@ -561,6 +566,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 value(o, vf, PA);
             }
         }
+        // The next item is taken only now, when this workgroup is about to be free: taking it
+        // earlier would hand out the queue's large items before it is known which workgroup
+        // finishes first.  The atomic's latency passes under the output stores.
+        if (wave == 0) k_next = pop();
         store_rows(o, m, l);
         if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();
