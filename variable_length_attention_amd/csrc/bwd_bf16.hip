@@ -7,21 +7,27 @@
 //     dV = P^T dO,   dS = P * (dO V^T - delta),   dQ = scale dS K,   dK = scale dS^T Q,
 // dK and dV summed over the query heads that share a key/value head.
 //
-// Two kernels, no atomics, so every gradient is deterministic:
-//   * dQ kernel, query-major (one item = 32 rows x 4 query heads, a wave per head):
-//         S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
-//     Rows live in lanes (as in the forward), so lse and delta are one value per lane and dS^T
-//     is already the B operand of the last product; K^T comes from transposing LDS reads.  It
-//     also computes delta from dO and O and writes it, with lse in log2 units, head-major
-//     ([2][H][T]: rows of one head contiguous) for the second kernel.
-//   * dK/dV kernel, key-major (one item = 128 keys of one key/value head, 32 keys per wave):
+// A row-values pass and one persistent kernel with two bodies, no atomics on gradients, so
+// every gradient is deterministic:
+//   * row values: lse in log2 units and delta = rowsum(dO * O) of every (row, head), written
+//     head-major ([2][H][T]: rows of one head contiguous) for the dK/dV body;
+//   * dK/dV body, key-major (one item = 128 keys of one key/value head, 32 keys per wave):
 //         S = Q K^T,  dP = dO V^T,  dS = P * (dP - delta),  dV += P^T dO,  dK += dS^T Q,
 //     for every 32-row unit of the sequence at or after the keys and every query head of the
 //     group.  Keys live in lanes, so P and dS are directly the A operands of the two
 //     accumulating products; dO and Q come from transposing LDS reads.  Software-pipelined
-//     like the forward (see the kernel).
+//     like the forward (see the body);
+//   * dQ body, query-major (one item = 32 rows x 4 query heads, a wave per head):
+//         S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
+//     Rows live in lanes (as in the forward), so lse and delta are one value per lane (delta
+//     recomputed from the rows it loads) and dS^T is already the B operand of the last
+//     product; K^T comes from transposing LDS reads.
+// The kernel drains the dK/dV queue first and the dQ queue after it, so that workgroups left
+// without dK/dV items while the largest ones finish take dQ items instead of idling.
 // The score products are recomputed in both kernels (seven products per pair instead of five):
 // the price of keeping dS out of memory and dQ free of atomics.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace hdp {
@@ -29,8 +35,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnit = 32;          // keys (dQ kernel) or rows (dK/dV kernel) per step
-constexpr int kStage = 64;         // keys per K/V stage of the dQ kernel
+constexpr int kUnit = 32;          // keys (dQ body) or rows (dK/dV body) per step
+constexpr int kStage = 64;         // keys per K/V stage of the dQ body
 constexpr int kStages = 3;
 constexpr int kKeyTile = 128;      // keys per dK/dV item
 
@@ -95,7 +101,7 @@ __device__ inline void dma_block(const uint16_t* src, int64_t stride, int64_t ba
 __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 // =============================================================================================
-// dQ kernel
+// dQ body
 // =============================================================================================
 // MODE 0: packed sequences (rows and keys of one sequence, causal); MODE 1: one ring step, the
 // slice's rows [Lq] against one chunk's keys [Lk] at a position offset, adding this chunk's
@@ -107,13 +113,16 @@ __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // v
 // arrive through direct global->LDS loads in a ring of three 64-key stages; K and V rows are
 // read for the products of unit u+1 at the start of a step, the transposed K fragments of
 // unit u once the dQ product of unit u-1 has been issued.
+template <int D>
+constexpr int dq_lds_bytes() { return kStages * 2 * kStage * Cfg<D>::kRowBytes + 8 * (int)sizeof(int); }
+
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
+__device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& args, unsigned char* lds, int* counters) {
     using C = Cfg<D>;
     constexpr int kTile = kStage * C::kRowBytes;
     constexpr int kBPW = kStage / C::kRowsPerBlock / kWaves;   // 1 KB stage loads per wave and tile
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][kTile];
-    __shared__ int s_item[8];
+    auto smem = (unsigned char (*)[2][kTile])lds;              // [kStages][K, V][tile]
+    int* s_item = (int*)(lds + kStages * 2 * kTile);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -127,7 +136,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     const int queue = blockIdx.x % args.nqueues_q;
     const int64_t q_stride = (int64_t)H * D, kv_stride = (int64_t)Hkv * D;
     const float c2 = args.scale_log2;
-    const int Trv = MODE == 0 ? args.T : args.Lq;  // row stride of the lse2/delta planes
     const bool causal = MODE == 0 ? true : (args.causal != 0);
     const int dpos = MODE == 0 ? 0 : args.dpos;    // query position minus key position
 
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
     };
     auto pop = [&]() {
         int k = 0;
-        if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
+        if (lane == 0) k = atomicAdd(&counters[queue * kQueueStride], 1);
         return k;
     };
     if (wave == 0) publish(__shfl(pop(), 0), 0);
@@ -245,7 +253,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         }
         const float delta = xhalf_sum(dpart);
         const float lse2 = row_ok ? args.lse[(base + row) * H + head] * kLog2e : 0.f;
-        if (row_ok) args.rowvals[((int64_t)half * H + head) * Trv + base + row] = half == 0 ? lse2 : delta;
         wait_vm0();
         __syncthreads();
 
@@ -420,11 +427,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
         if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();
     }
-    if (tid == 0) queue_finish(args.counters);
 }
 
 // =============================================================================================
-// dK/dV kernel
+// dK/dV body
 // =============================================================================================
 // Item = 128 keys of one key/value head (wave w owns keys 32w..32w+31 of the tile, as the B
 // operand: K^T and V^T fragments stay in registers).  Its steps walk the stages (row unit of 32
@@ -433,8 +439,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs args) {
 // around the elementwise part of stage st (P = exp2(S c - lse2), dS = P (dP - delta)), one
 // element per slot.  Q and dO tiles (32 rows each) and the stage's 32 lse2 and delta values
 // arrive in LDS through direct global->LDS loads, in a ring of four stages two steps ahead.
+// eight stages of a Q tile, a dO tile (32 rows each) and the 32 rows' lse2 and delta, plus the
+// two item slots (the layout is checked against the body's own in a static_assert)
+template <int D>
+constexpr int dkdv_lds_bytes() { return 8 * (2 * kUnit * Cfg<D>::kRowBytes + 2 * kUnit * 4) + 8 * (int)sizeof(int); }
+
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
+__device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& args, unsigned char* lds, int* counters) {
     using C = Cfg<D>;
     constexpr int kTile = kUnit * C::kRowBytes;           // 32 rows of Q or dO
     constexpr int kBlocks = kUnit / C::kRowsPerBlock;      // 1 KB loads per tile
@@ -453,8 +464,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         unsigned char d[kTile];
         float rv[2][kUnit];                                // lse2, delta of the 32 rows
     };
-    __shared__ __attribute__((aligned(1024))) Stage ring[kRing];
-    __shared__ int s_item[8];
+    static_assert(kRing * sizeof(Stage) + 8 * sizeof(int) == (size_t)dkdv_lds_bytes<D>(), "LDS layout");
+    Stage* ring = (Stage*)lds;
+    int* s_item = (int*)(lds + kRing * sizeof(Stage));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
     };
     auto pop = [&]() {
         int k = 0;
-        if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
+        if (lane == 0) k = atomicAdd(&counters[queue * kQueueStride], 1);
         return k;
     };
     if (wave == 0) publish(__shfl(pop(), 0), 0);
@@ -816,31 +828,87 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs args) {
         if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();
     }
-    if (tid == 0) queue_finish(args.counters);
+}
+
+// =============================================================================================
+// Row values and the combined kernel
+// =============================================================================================
+// lse in log2 units and delta = rowsum(dO * O) of every (row, head), into the head-major
+// [2][H][rows] workspace that the dK/dV stages load 32 rows at a time.  Sixteen lanes per (row,
+// head): lane c takes the 8 elements of 16-byte chunk c (consecutive lanes read consecutive
+// chunks, so a wave's loads are contiguous), then a butterfly over the 16 lanes sums them.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_rowvals_kernel(BwdArgs args) {
+    constexpr int kLanes = 16;                       // lanes per (row, head)
+    constexpr int kPerLane = D / kLanes;             // elements per lane: 8 (D = 128) or 4 (D = 64)
+    const int H = args.H;
+    const int rows = MODE == 0 ? args.T : args.Lq;
+    const int64_t n = (int64_t)rows * H;
+    const int c = threadIdx.x % kLanes;
+    for (int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kLanes; t < n;
+         t += (int64_t)gridDim.x * blockDim.x / kLanes) {
+        const uint16_t* dp = args.dout + t * D + c * kPerLane;
+        const uint16_t* op = args.out + t * D + c * kPerLane;
+        float part = 0.f;
+        if (kPerLane == 8) {
+            const u32x4 dv = *(const u32x4*)dp;
+            const u32x4 ov = *(const u32x4*)op;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(ov[e]), part);
+                part = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(ov[e]), part);
+            }
+        } else {
+            const u32x2 dv = *(const u32x2*)dp;
+            const u32x2 ov = *(const u32x2*)op;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                part = __builtin_fmaf(bf16_lo(dv[e]), bf16_lo(ov[e]), part);
+                part = __builtin_fmaf(bf16_hi(dv[e]), bf16_hi(ov[e]), part);
+            }
+        }
+#pragma unroll
+        for (int m = kLanes / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m, kLanes);
+        if (c == 0) {
+            const int64_t row = t / H;
+            const int head = (int)(t - row * H);
+            args.rowvals[(int64_t)head * rows + row] = args.lse[t] * kLog2e;
+            args.rowvals[((int64_t)H + head) * rows + row] = part;
+        }
+    }
+}
+
+// One persistent launch drains the dK/dV queue and then the dQ queue.  The dK/dV items (a key
+// tile with every row below its diagonal) are the larger ones, and on a skewed pack a few of
+// them outlast the rest of that queue; the workgroups that run out of dK/dV items start on dQ
+// items meanwhile, instead of idling until the next launch.
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs args) {
+    constexpr int kLds = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
+    dkdv_body<D, MODE>(args, lds, args.counters);
+    __syncthreads();
+    dq_body<D, MODE>(args, lds, args.counters + kCounterSetInts);
+    if (threadIdx.x == 0) queue_finish(args.counters);
+}
+
+template <int D, int MODE>
+hipError_t launch_bwd_t(const BwdArgs& a, int grid, hipStream_t s) {
+    const int64_t n = (int64_t)(MODE == 0 ? a.T : a.Lq) * a.H;
+    const int blocks = (int)std::min<int64_t>((n * 16 + 255) / 256, 8192);
+    hipLaunchKernelGGL((bwd_rowvals_kernel<D, MODE>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<D, MODE>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int D, int grid, hipStream_t s) {
-    if (D == 128) {
-        hipLaunchKernelGGL((bwd_dq_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, 0>), dim3(grid), dim3(kThreads), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((bwd_dq_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64, 0>), dim3(grid), dim3(kThreads), 0, s, a);
-    }
-    return hipGetLastError();
+    return D == 128 ? launch_bwd_t<128, 0>(a, grid, s) : launch_bwd_t<64, 0>(a, grid, s);
 }
 
 hipError_t launch_bwd_chunk(const BwdArgs& a, int D, int grid, hipStream_t s) {
-    if (D == 128) {
-        hipLaunchKernelGGL((bwd_dq_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((bwd_dq_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, s, a);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, s, a);
-    }
-    return hipGetLastError();
+    return D == 128 ? launch_bwd_t<128, 1>(a, grid, s) : launch_bwd_t<64, 1>(a, grid, s);
 }
 
 }  // namespace hdp

@@ -254,12 +254,13 @@ __device__ inline bool queue_decode(const int32_t* cu, int n_seq, const QueuePla
 }
 
 // Called by thread 0 of every workgroup after its last pop: the last one out resets the
-// counters, so they are zero again for the next launch on the stream.
+// queue counters of both sets, so they are zero again for the next launch on the stream.
 __device__ inline void queue_finish(int* counters) {
     __threadfence();
     int* done = &counters[kMaxQueues * kQueueStride];
     if (atomicAdd(done, 1) == (int)gridDim.x - 1) {
-        for (int qi = 0; qi < kMaxQueues; ++qi) atomicExch(&counters[qi * kQueueStride], 0);
+        for (int set = 0; set < 2; ++set)
+            for (int qi = 0; qi < kMaxQueues; ++qi) atomicExch(&counters[set * kCounterSetInts + qi * kQueueStride], 0);
         atomicExch(done, 0);
         __threadfence();
     }

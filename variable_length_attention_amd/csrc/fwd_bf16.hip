@@ -134,9 +134,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     }
 
     // ---- item queue (wave 0) ----
-    // Item k of this workgroup's queue -> s_item[slot].  The next index is popped when an item
-    // starts and decoded when it ends, so neither the atomic's latency nor the decode sits
-    // between items; two slots, because a slow wave may still read the current item's slot.
+    // Item k of this workgroup's queue -> s_item[slot].  The next index is popped at the end of
+    // an item (just before its output stores, which hide the atomic's latency) and decoded once
+    // the stores are issued; two slots, because a slow wave may still read the current item's
+    // slot.
     auto publish = [&](int k, int slot) {
         int a = 0, len = 0, hbq = 0, c = 0;
         bool ok = k < plan.total;

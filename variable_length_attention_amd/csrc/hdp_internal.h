@@ -7,10 +7,13 @@
 namespace hdp {
 
 // Work-queue counters: one per XCD queue plus a completion counter, each on its own 128-byte
-// line.  The last workgroup of a launch resets them, so they are zero between launches.
+// line, in two sets (the backward kernel drains two queues one after the other; set 1 has no
+// completion counter of its own).  The last workgroup of a launch resets them, so they are
+// zero between launches.
 constexpr int kQueueStride = 32;                 // ints between counters
 constexpr int kMaxQueues = 8;                    // one queue per XCD
-constexpr int kCounterInts = (kMaxQueues + 1) * kQueueStride;
+constexpr int kCounterSetInts = (kMaxQueues + 1) * kQueueStride;
+constexpr int kCounterInts = 2 * kCounterSetInts;
 
 struct FwdArgs {
     const uint16_t* q;      // [rows][H][D] bf16
@@ -67,8 +70,8 @@ struct BwdArgs {
     int32_t H, Hkv;
     float scale;
     float scale_log2;
-    float* rowvals;         // [2][H][T] workspace written by the dQ kernel: lse * log2(e) and
-                            // delta = rowsum(dO * out), rows of one head contiguous
+    float* rowvals;         // [2][H][T] workspace written by the row-values pass: lse * log2(e)
+                            // and delta = rowsum(dO * out), rows of one head contiguous
     uint16_t* dq;           // varlen: bf16 [T][H][D]
     uint16_t* dk;           // varlen: bf16 [T][Hkv][D]
     uint16_t* dv;
