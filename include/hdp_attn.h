@@ -32,9 +32,9 @@
  *     outside rows 0 .. cu[n_seq]-1.  Rows outside [cu[0], cu[n_seq]) are left untouched.
  *   - Supported head dims: D = 64 and D = 128 (else HDP_ERR_UNSUPPORTED).
  *   - The library owns one small workspace per device (work-queue counters and, for the
- *     backward, every row's lse and delta as fp32, 2 x rows x H), grown on demand.  Calls that overlap in time on one
- *     device (different streams or host threads) share it and must not run concurrently.
- *     hdp_release_workspace() frees it.
+ *     backward, every row's lse and delta as fp32, 2 x rows x H), grown on demand.  Calls that
+ *     overlap in time on one device (different streams or host threads) share it and must not
+ *     run concurrently.  hdp_release_workspace() frees it.
  */
 #ifndef HDP_ATTN_H
 #define HDP_ATTN_H
