@@ -72,7 +72,10 @@ template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][C::kTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char obuf[kWaves][32 * kStageRowBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char obuf[kWaves][32 * kStageRowBytes];
+    // a wave's Q staging tile (64 rows) fits a ring buffer and two output tiles
+    static_assert(kRowsPerWave * C::kRowBytes <= C::kTileBytes && kRowsPerWave * C::kRowBytes <= 2 * 32 * kStageRowBytes,
+                  "Q staging");
     __shared__ int s_item[8];
 
     const int tid = threadIdx.x;
@@ -192,17 +195,64 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         const int n_units = (wg_rmax < 0 || jmax < 0) ? 0 : (int)(jmax / kUnit) + 1;
         const int n_stages = (n_units + 1) / 2;
 
-        // ---- Q^T fragments in registers ----
+        // ---- Q^T fragments in registers, loaded through LDS ----
+        // The wave's 64 query rows arrive by direct loads (16 lanes per row, so every load reads
+        // whole 256-byte rows) into a staging tile laid out like a K stage, and the fragments
+        // are then read as the K fragments are: loading the fragments straight from memory,
+        // where each lane reads its own row, takes ≈2K cycles longer per item.  The staging
+        // tiles are ring buffer 2 (waves 0-1), which the first stage turn refills, and the
+        // output tiles (waves 2-3), which the epilogue reuses.  Rows past the sequence's end
+        // repeat its last row (their results are never stored).
         u32x4 qf[kNT][C::kKS];
+        unsigned char* qstage = wave < 2 ? smem[2][wave] : obuf[2 * (wave - 2)];
+        auto load_q = [&]() {
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const int row = r_lo + nt * 32 + l32;
-            const bool ok = row < s_rows;
-            const uint16_t* qp = args.q + (qbase + row) * q_stride + (int64_t)head * D + half * 8;
+            for (int i = 0; i < kRowsPerWave / C::kRowsPerBlock; ++i) {
+                const int row = i * C::kRowsPerBlock + lane / C::kChunks;
+                const int chunk = (lane % C::kChunks) ^ swz(row);
+                const int r = min(r_lo + row, s_rows - 1);
+                lds_dma16(args.q + (qbase + r) * q_stride + (int64_t)head * D + chunk * 8, lds_addr(qstage + i * 1024));
+            }
+        };
+        // The fragments go to accumulation registers (AGPRs), which the score product reads as
+        // its B operand, through one assembly block that also waits for the reads; left to
+        // itself the register allocator moves other operands there and adds copies to every
+        // step.
+        auto read_q = [&]() {
 #pragma unroll
-            for (int ks = 0; ks < C::kKS; ++ks)
-                qf[nt][ks] = ok ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
-        }
+            for (int nt = 0; nt < kNT; ++nt) {
+                const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(qstage) + nt * 32 * C::kRowBytes));
+                uint32_t a[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j] = lds_add(b, kofs[j]);
+                if constexpr (C::kKS == 8) {
+                    asm volatile(
+                        "ds_read_b128 %0, %8\n\t"
+                        "ds_read_b128 %1, %9\n\t"
+                        "ds_read_b128 %2, %10\n\t"
+                        "ds_read_b128 %3, %11\n\t"
+                        "ds_read_b128 %4, %8 offset:128\n\t"
+                        "ds_read_b128 %5, %9 offset:128\n\t"
+                        "ds_read_b128 %6, %10 offset:128\n\t"
+                        "ds_read_b128 %7, %11 offset:128\n\t"
+                        "s_waitcnt lgkmcnt(0)"
+                        : "=a"(qf[nt][0]), "=a"(qf[nt][1]), "=a"(qf[nt][2]), "=a"(qf[nt][3]),
+                          "=a"(qf[nt][4]), "=a"(qf[nt][5]), "=a"(qf[nt][6]), "=a"(qf[nt][7])
+                        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                        : "memory");
+                } else {
+                    asm volatile(
+                        "ds_read_b128 %0, %4\n\t"
+                        "ds_read_b128 %1, %5\n\t"
+                        "ds_read_b128 %2, %6\n\t"
+                        "ds_read_b128 %3, %7\n\t"
+                        "s_waitcnt lgkmcnt(0)"
+                        : "=a"(qf[nt][0]), "=a"(qf[nt][1]), "=a"(qf[nt][2]), "=a"(qf[nt][3])
+                        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                        : "memory");
+                }
+            }
+        };
 
         // Per-row visibility limit: key j (relative to key 0) is visible to this lane's row of
         // column tile nt iff j <= lim0[nt] (causal) and j < sk.
@@ -350,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             if (n_units > 0) {
                 load_stage(0, 0);
                 if (n_stages > 1) load_stage(1, 1);
+                load_q();
                 __builtin_amdgcn_s_waitcnt(0x0F70);
             }
             __syncthreads();
@@ -547,6 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 PA[nt][0] = bf16x8{};
                 PA[nt][1] = bf16x8{};
             }
+            read_q();
             {
                 u32x4 kf[C::kKS];
                 read_k(0, kf);
