@@ -19,9 +19,8 @@
 //     like the forward (see the body);
 //   * dQ body, query-major (one item = 32 rows x 4 query heads, a wave per head):
 //         S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - delta),  dQ^T += K^T dS^T.
-//     Rows live in lanes (as in the forward), so lse and delta are one value per lane (delta
-//     recomputed from the rows it loads) and dS^T is already the B operand of the last
-//     product; K^T comes from transposing LDS reads.
+//     Rows live in lanes (as in the forward), so lse and delta are one value per lane and dS^T
+//     is already the B operand of the last product; K^T comes from transposing LDS reads.
 // The kernel drains the dK/dV queue first and the dQ queue after it, so that workgroups left
 // without dK/dV items while the largest ones finish take dQ items instead of idling.
 // The score products are recomputed in both kernels (seven products per pair instead of five):
@@ -234,25 +233,19 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             if (n_stages > 1) load_stage(1);
         }
 
-        // Q^T and dO^T fragments, delta = rowsum(dO * O), lse in log2 units
+        // Q^T and dO^T fragments; lse in log2 units and delta from the row-values pass
         u32x4 qf[C::kKS], df[C::kKS];
-        float dpart = 0.f;
         {
             const int64_t off = (base + row) * q_stride + (int64_t)head * D + half * 8;
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks) {
                 qf[ks] = row_ok ? *(const u32x4*)(args.q + off + ks * 16) : u32x4{0, 0, 0, 0};
                 df[ks] = row_ok ? *(const u32x4*)(args.dout + off + ks * 16) : u32x4{0, 0, 0, 0};
-                const u32x4 of = row_ok ? *(const u32x4*)(args.out + off + ks * 16) : u32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dpart = __builtin_fmaf(bf16_lo(df[ks][e]), bf16_lo(of[e]), dpart);
-                    dpart = __builtin_fmaf(bf16_hi(df[ks][e]), bf16_hi(of[e]), dpart);
-                }
             }
         }
-        const float delta = xhalf_sum(dpart);
-        const float lse2 = row_ok ? args.lse[(base + row) * H + head] * kLog2e : 0.f;
+        const int Trv = MODE == 0 ? args.T : args.Lq;    // row stride of the lse2/delta planes
+        const float lse2 = row_ok ? args.rowvals[(int64_t)head * Trv + base + row] : 0.f;
+        const float delta = row_ok ? args.rowvals[((int64_t)H + head) * Trv + base + row] : 0.f;
         wait_vm0();
         __syncthreads();
 
