@@ -137,11 +137,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     }
 
     // ---- item queue (wave 0) ----
-    // Item k of this workgroup's queue -> s_item[slot].  The next index is popped at the end of
-    // an item (just before its output stores, which hide the atomic's latency) and decoded once
-    // the stores are issued; two slots, because a slow wave may still read the current item's
-    // slot.
+    // Item k of queue src_q -> s_item[slot].  The next index is popped at the end of an item
+    // (just before its output stores, which hide the atomic's latency) and decoded once the
+    // stores are issued; two slots, because a slow wave may still read the current item's slot.
+    // Every queue holds the same items (for its own head blocks).  A workgroup whose queue is
+    // empty takes the remaining items of the other XCDs' queues in turn: the XCDs do not all
+    // run at the same speed, and otherwise the launch waits for the slowest one's queue.
+    int src_q = queue;
+    int stolen = 0;
+    auto pop = [&]() {
+        int k = 0;
+        if (lane == 0) k = atomicAdd(&args.counters[src_q * kQueueStride], 1);
+        return k;
+    };
     auto publish = [&](int k, int slot) {
+        while (k >= plan.total && stolen < nq_queues - 1) {
+            ++stolen;
+            src_q = (queue + stolen) % nq_queues;
+            k = __shfl(pop(), 0);
+        }
         int a = 0, len = 0, hbq = 0, c = 0;
         bool ok = k < plan.total;
         if (ok) {
@@ -157,14 +171,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         if (lane == 0) {
             s_item[4 * slot + 0] = ok ? a : -1;
             s_item[4 * slot + 1] = len;
-            s_item[4 * slot + 2] = queue + nq_queues * hbq;
+            s_item[4 * slot + 2] = src_q + nq_queues * hbq;
             s_item[4 * slot + 3] = c - 1;                 // query tile group: cost grows with it
         }
-    };
-    auto pop = [&]() {
-        int k = 0;
-        if (lane == 0) k = atomicAdd(&args.counters[queue * kQueueStride], 1);
-        return k;
     };
     if (wave == 0) publish(__shfl(pop(), 0), 0);
     __syncthreads();
