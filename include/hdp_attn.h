@@ -30,7 +30,8 @@
  *     T = cu[n_seq]).  Its contents are not checked on the host; the kernels clamp every
  *     sequence to [0, cu[n_seq]], so malformed entries give empty sequences, never an access
  *     outside rows 0 .. cu[n_seq]-1.  Rows outside [cu[0], cu[n_seq]) are left untouched.
- *   - Supported head dims: D = 64 and D = 128 (else HDP_ERR_UNSUPPORTED).
+ *   - Supported head dims: D = 64 and D = 128 (else HDP_ERR_UNSUPPORTED); head counts
+ *     H <= 65535 (else HDP_ERR_OVERFLOW).
  *   - The library owns one small workspace per device (work-queue counters and, for the
  *     backward, every row's lse and delta as fp32, 2 x rows x H), grown on demand.  Calls that
  *     overlap in time on one device (different streams or host threads) share it and must not

@@ -114,6 +114,7 @@ def fwd(**kw):
     (dict(q=NULL), _lib.HDP_ERR_INVALID_ARG),
     (dict(cu=NULL), _lib.HDP_ERR_INVALID_ARG),
     (dict(lse=NULL), _lib.HDP_ERR_INVALID_ARG),
+    (dict(H=65544, Hkv=8), _lib.HDP_ERR_OVERFLOW),
     (dict(n_seq=0, q=NULL, out=NULL), _lib.HDP_OK),  # empty work is a no-op
 ])
 def test_varlen_fwd_validation(kw, status):

@@ -68,9 +68,12 @@ int ensure_workspace(DeviceState* st, size_t bytes) {
 
 bool head_dim_ok(int D) { return D == 64 || D == 128; }
 
+// Head counts above 65535 would let an output tile's byte range (32 rows of H heads) reach the
+// kernels' drop offset for bounds-checked stores.
 int check_heads(int32_t H, int32_t Hkv, int32_t D) {
     if (H <= 0 || Hkv <= 0 || D <= 0 || H % Hkv != 0) return HDP_ERR_INVALID_ARG;
     if (!head_dim_ok(D)) return HDP_ERR_UNSUPPORTED;
+    if (H > 65535) return HDP_ERR_OVERFLOW;
     return HDP_OK;
 }
 

@@ -122,7 +122,9 @@ __device__ inline void buf_store_b128(void* base, uint32_t bytes, uint32_t off, 
 __device__ inline void buf_store_b32(void* base, uint32_t bytes, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), uniform_rsrc(base, bytes), off, 0, 0);
 }
-constexpr uint32_t kDropOffset = 0x40000000u;   // beyond every resource the kernels build
+// Beyond every resource the kernels build: the largest covers 32 rows of H <= 65535 heads of
+// 512-byte rows, under 2^30 bytes.
+constexpr uint32_t kDropOffset = 0x80000000u;
 
 // Two floats to two bf16 (round to nearest even) in one dword, first in the low half.
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
