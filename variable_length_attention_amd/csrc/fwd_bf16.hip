@@ -38,9 +38,9 @@
 // in order of decreasing cost, where the cost of a query tile is the number of key tiles it
 // visits (the tile form of the O(s^2) cost of hdp_seq_flops): longest-processing-time first, so
 // short items fill the gaps at the end instead of idling CUs.  With 8 head blocks there is one
-// queue per XCD and head block b is served only by the XCD b mod 8, so each K/V head's tiles
-// stay in one XCD's L2.  The order is decoded on the device from cu_seqlens, without a
-// planning launch.
+// queue per XCD and head block b is served by the XCD b mod 8, so each K/V head's tiles stay in
+// one XCD's L2, until that XCD's queue is empty: its workgroups then help with the other
+// queues.  The order is decoded on the device from cu_seqlens, without a planning launch.
 #include "device_common.h"
 
 namespace hdp {
