@@ -81,6 +81,14 @@ def test_future_chunk_adds_nothing_and_accumulators_are_updated_in_place():
     dq, dk, dv = run_gpu(q, k, v, 0, Lq, True, 0.1, out, lse, do, init=init)
     for g, i in zip((dq, dk, dv), init):
         assert torch.equal(g.cpu(), i)
+    # the same with rows that saw no key at all anywhere (lse = -inf, out = 0): still nothing added
+    lse_empty = lse.clone()
+    lse_empty[::3] = -float("inf")
+    out_empty = out.clone()
+    out_empty[::3] = 0
+    dq, dk, dv = run_gpu(q, k, v, 0, Lq, True, 0.1, out_empty, lse_empty, do, init=init)
+    for g, i in zip((dq, dk, dv), init):
+        assert torch.equal(g.cpu(), i)
     # a visible chunk: result = initial value + this chunk's share
     q_off = 500
     k_all, v_all = bf16(rng, (q_off + Lq, Hkv, D)), bf16(rng, (q_off + Lq, Hkv, D))
@@ -90,6 +98,26 @@ def test_future_chunk_adds_nothing_and_accumulators_are_updated_in_place():
     rq, rk, rv = oracle.chunk_bwd(q, k2, v2, q_off, 200, True, 0.1, out2, lse2, do)
     for g, r, i in ((dq, rq, init[0]), (dk, rk, init[1]), (dv, rv, init[2])):
         grad_close(g.cpu() - i, r)
+
+
+def test_rows_that_see_no_key_contribute_nothing():
+    # keys start 40 positions after the slice: rows 0..39 see no key of this chunk (nor any other
+    # here), so the forward gives them out = 0 and lse = -inf; the row tiles that hold them also
+    # hold rows that do see keys, so they go through the kernel with every pair masked
+    rng = np.random.default_rng(78)
+    Lq, Lk, H, Hkv, D = 96, 80, 8, 2, 128
+    q, do = bf16(rng, (Lq, H, D)), bf16(rng, (Lq, H, D))
+    k, v = bf16(rng, (Lk, Hkv, D)), bf16(rng, (Lk, Hkv, D))
+    o, l = oracle.chunk_partial(q, k, v, 0, 40, True, 0.1)
+    assert np.isneginf(l[:40]).all() and np.isfinite(l[40:]).all()
+    out = torch.from_numpy(o).to(torch.bfloat16)
+    lse = torch.from_numpy(l).to(torch.float32)
+    dq, dk, dv = run_gpu(q, k, v, 0, 40, True, 0.1, out, lse, do)
+    rq, rk, rv = oracle.chunk_bwd(q, k, v, 0, 40, True, 0.1, out, lse, do)
+    for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        assert torch.isfinite(g).all()
+        grad_close(g.cpu(), r)
+    assert (dq[:40] == 0).all()
 
 
 def test_ring_of_chunks_sums_to_the_packed_backward():

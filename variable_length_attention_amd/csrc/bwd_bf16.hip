@@ -843,7 +843,7 @@ __global__ __launch_bounds__(256) void bwd_rowvals_kernel(BwdArgs args) {
         const uint16_t* dp = args.dout + t * D + c * kPerLane;
         const uint16_t* op = args.out + t * D + c * kPerLane;
         float part = 0.f;
-        if (kPerLane == 8) {
+        if constexpr (kPerLane == 8) {
             const u32x4 dv = *(const u32x4*)dp;
             const u32x4 ov = *(const u32x4*)op;
 #pragma unroll
@@ -865,7 +865,9 @@ __global__ __launch_bounds__(256) void bwd_rowvals_kernel(BwdArgs args) {
         if (c == 0) {
             const int64_t row = t / H;
             const int head = (int)(t - row * H);
-            args.rowvals[(int64_t)head * rows + row] = args.lse[t] * kLog2e;
+            // a row that saw no key at all (lse = -inf) gets +inf, so that every P of it is 0
+            const float l = args.lse[t];
+            args.rowvals[(int64_t)head * rows + row] = l == -INFINITY ? INFINITY : l * kLog2e;
             args.rowvals[((int64_t)H + head) * rows + row] = part;
         }
     }
