@@ -138,7 +138,6 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
     bms, _ = timed_launches(ring_bwd_step, rs, max(2, warmup // 10), torch)
     fb = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D, 1) for c in range(w.n_chunks))
     out["ring_chunks_128k"] = {"ms_per_step": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
-                               "frac_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "merge_us": merge_ms * 1e3,
                                "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
                                "bwd_ms_per_step": bms, "bwd_TFLOP/s": fb / (bms * 1e-3) / 1e12}
@@ -213,6 +212,18 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
         fl = sum(ops.hdp_seq_flops(s, w.H, w.D) for s in w.lengths)
         out[w.name] = {"n_seq": len(w.lengths), "GFLOP": fl / 1e9, "kernel_us": ms * 1e3,
                        "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+    # every throughput also as a fraction of its roofline: TFLOP/s against the bf16 MFMA peak,
+    # GB/s against HBM
+    def add_fracs(row):
+        for key in list(row):
+            if isinstance(row[key], dict):
+                add_fracs(row[key])
+            elif key.endswith("TFLOP/s"):
+                row[key[:-len("TFLOP/s")] + "frac_bf16_peak"] = row[key] / PEAK_BF16_TFLOPS
+            elif key.endswith("GB/s"):
+                row[key[:-len("GB/s")] + "frac_hbm"] = row[key] / PEAK_HBM_GBS
+    for row in out.values():
+        add_fracs(row)
     return out
 
 
