@@ -35,7 +35,9 @@
  *   - The library owns one small workspace per device (work-queue counters and, for the
  *     backward, every row's lse and delta as fp32, 2 x rows x H), grown on demand.  Calls that
  *     overlap in time on one device (different streams or host threads) share it and must not
- *     run concurrently.  hdp_release_workspace() frees it.
+ *     run concurrently.  hdp_release_workspace() frees it.  For tests of the error path, a
+ *     set environment variable HDP_TEST_FAIL_ALLOC makes every growth of the workspace fail
+ *     (HDP_ERR_HIP, nothing launched).
  */
 #ifndef HDP_ATTN_H
 #define HDP_ATTN_H

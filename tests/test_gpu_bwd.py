@@ -53,6 +53,25 @@ def test_backward_small_packs_full(lengths, H, Hkv, D):
               % (lengths, H, Hkv, D, name, *e))
 
 
+def test_failed_workspace_allocation_is_reported_and_the_next_call_recovers(monkeypatch):
+    # HDP_TEST_FAIL_ALLOC makes the library's workspace allocator fail when the workspace has to
+    # grow; releasing it first forces the growth.  The call must return HDP_ERR_HIP without
+    # launching anything, and the next call, with allocation working again, must be correct.
+    from variable_length_attention_amd import _lib
+    w, q, k, v, do, cu = case([70, 31, 160], 4, 2, 128, seed=41)
+    torch.cuda.synchronize()
+    ops.hdp_release_workspace()
+    monkeypatch.setenv("HDP_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(_lib.HdpError) as err:
+        run_fwd_bwd(w, q, k, v, do, cu)
+    assert err.value.status == _lib.HDP_ERR_HIP
+    monkeypatch.delenv("HDP_TEST_FAIL_ALLOC")
+    dq, dk, dv = run_fwd_bwd(w, q, k, v, do, cu)
+    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, w.scale)
+    for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        grad_close(g, r)
+
+
 def test_backward_more_than_64_sequences_full():
     # long sequences at index 64 and later: their spans come from memory in the work queue
     rng = np.random.default_rng(42)
