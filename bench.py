@@ -3,8 +3,9 @@
 Headline: causal varlen attention forward on one rank's 8192-token packed slice (skewed length
 mix; GQA 32 query / 8 key-value heads; D = 128; bf16), as TFLOP/s of exact algorithmic FLOPs
 (hdp_seq_flops: 4*H*D per visible (query, key) pair) and as a fraction of the bf16 dense MFMA
-peak.  Method: W untimed warm-up steps, then K timed steps (defaults 20 and 200, the pages'
-own method: mean of 200 iterations after 20 warm-up), bracketed by device synchronisation.
+peak.  Method: about a second of untimed launches of the same step (the GPU reaches its steady
+clock), then W untimed warm-up steps, then K timed steps (defaults 20 and 200, the pages' own
+method: mean of 200 iterations after 20 warm-up), bracketed by device synchronisation.
 One step = one call of hdp_attn_varlen_fwd over the resident slice.
 
 Printed: one JSON line (rank 0).  `roofline.achieved` is the FLOPs of one launch divided by the
@@ -12,7 +13,9 @@ kernel's mean duration from per-launch HIP events on the launch stream; `rooflin
 the HBM byte count per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded under
 profiles/ (null if absent or taken on a different kernel source).  `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same slice on the host cores.  `detail` adds the other
-rows of the hot path (ring chunks + LSE merge, 32K micro-batches, backward) for context.
+rows of the hot path (ring chunks + LSE merge, 32K micro-batches, backward) for context; each
+of them times at least 50 launches and at least 100 ms, whatever --steps says, and reports
+per-launch mean / min / median / max.
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+NOMINAL_MHZ = 2400.0          # the clock the bf16 peak is quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_packed_slice_8k.json")
 # the forward kernel's sources: counters taken on another version of them do not apply
 FWD_SRC = [os.path.join(ROOT, "variable_length_attention_amd", "csrc", f)
@@ -57,7 +61,9 @@ def load_traffic():
 
 
 def timed_launches(fn, steps: int, warmup: int, torch):
-    """Runs fn() warmup+steps times; returns (ms per step over the bracket, mean per-launch ms)."""
+    """Runs fn() warmup+steps times.  Returns the mean ms per step over the bracket (device
+    synchronised on both sides) and per-launch statistics from HIP events recorded around each
+    call on the stream the kernels run on (torch's current stream)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -73,8 +79,38 @@ def timed_launches(fn, steps: int, warmup: int, torch):
         ends[i].record()
     outer1.record()
     torch.cuda.synchronize()
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return outer0.elapsed_time(outer1) / steps, sum(per) / len(per)
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return {"ms_step": outer0.elapsed_time(outer1) / steps, "launches": steps,
+            "mean_ms": sum(per) / len(per), "min_ms": per[0], "median_ms": per[len(per) // 2],
+            "max_ms": per[-1]}
+
+
+def timed_floor(fn, torch, min_launches: int = 50, min_ms: float = 100.0, warmup: int = 3):
+    """timed_launches with at least min_launches launches and at least min_ms of timed work,
+    whatever --steps says (a few launches are timed first to size the run)."""
+    probe = timed_launches(fn, 3, warmup, torch)
+    n = max(min_launches, int(math.ceil(min_ms / max(probe["mean_ms"], 1e-3))))
+    return timed_launches(fn, n, 2, torch)
+
+
+def settle_clock(fn, torch, ms: float) -> dict:
+    """Untimed launches of the headline step for about `ms` of wall time, so that the GPU has
+    reached its steady clock under this load before the warm-up and timed steps begin."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            fn()
+        n += 20
+        torch.cuda.synchronize()
+    return {"settle_launches": n, "settle_ms": round((time.perf_counter() - t0) * 1e3, 1)}
+
+
+def us_stats(t: dict) -> dict:
+    return {"launches": t["launches"], "mean_us": round(t["mean_ms"] * 1e3, 2),
+            "min_us": round(t["min_ms"] * 1e3, 2), "median_us": round(t["median_ms"] * 1e3, 2),
+            "max_us": round(t["max_ms"] * 1e3, 2)}
 
 
 def cpu_baseline(w, q, k, v, cu):
@@ -96,7 +132,7 @@ def cpu_baseline(w, q, k, v, cu):
                       "mean %.2f s per pass" % (flops, len(times), dt)}
 
 
-def detail_rows(torch, ops, synth, steps: int, warmup: int):
+def detail_rows(torch, ops, synth):
     """Other rows of the hot path, timed the same way (context, not the headline)."""
     out = {}
     # ring-chunk share: 16 chunk partials + 15 LSE merges
@@ -116,10 +152,11 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
                                        w.scale, o_partial=po, lse=pl)
             ops.hdp_lse_merge(acc_o, acc_l, po, pl)
 
-    rs = max(5, steps // 20)
-    ms, _ = timed_launches(ring_step, rs, max(2, warmup // 10), torch)
+    t_ring = timed_floor(ring_step, torch)
+    ms = t_ring["ms_step"]
     fl = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D) for c in range(w.n_chunks))
-    _, merge_ms = timed_launches(lambda: ops.hdp_lse_merge(acc_o, acc_l, po, pl), steps, warmup, torch)
+    t_merge = timed_floor(lambda: ops.hdp_lse_merge(acc_o, acc_l, po, pl), torch, min_launches=200)
+    merge_ms = t_merge["mean_ms"]
     merge_bytes = w.q_len * w.H * (12 * w.D + 12)
     # the share's backward: 16 chunk backward steps into fp32 accumulators, given the merged
     # forward result (out rounded to bf16, lse) and a seeded dO
@@ -135,12 +172,16 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
             ops.hdp_attn_chunk_bwd(q, chunks[c][0], chunks[c][1], w.q_offset, c * L, out_bf16, acc_l,
                                    dout, dq_acc, dk_acc, dv_acc, causal=True, scale=w.scale)
 
-    bms, _ = timed_launches(ring_bwd_step, rs, max(2, warmup // 10), torch)
+    t_rbwd = timed_floor(ring_bwd_step, torch, min_launches=20)
+    bms = t_rbwd["ms_step"]
     fb = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D, 1) for c in range(w.n_chunks))
     out["ring_chunks_128k"] = {"ms_per_step": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
+                               "step": us_stats(t_ring),
                                "merge_us": merge_ms * 1e3,
                                "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
-                               "bwd_ms_per_step": bms, "bwd_TFLOP/s": fb / (bms * 1e-3) / 1e12}
+                               "merge": us_stats(t_merge),
+                               "bwd_ms_per_step": bms, "bwd_TFLOP/s": fb / (bms * 1e-3) / 1e12,
+                               "bwd_step": us_stats(t_rbwd)}
     del q, k, v, chunks, acc_o, acc_l, po, pl, out_bf16, dout, dq_acc, dk_acc, dv_acc
     # the same 128K sequence over the same 16 ranks with front/back chunk pairing: rank k holds
     # query chunks k and 31-k (4096 tokens each) and meets all 32 chunks; every rank does the
@@ -177,10 +218,12 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
                                                qo, ko, True, w.scale, o_partial=po_, lse=pl_)
                     ops.hdp_lse_merge(ao, al, po_, pl_)
 
-        pms, _ = timed_launches(pair_step, rs, max(2, warmup // 10), torch)
+        t_pair = timed_floor(pair_step, torch)
+        pms = t_pair["ms_step"]
         pfl = sum(ops.hdp_chunk_flops(ql, kl, qo, ko, True, w.H, w.D) for _, qo, ql, ko, kl in steps_)
         pair_rows["rank%d" % rank] = {"ms_per_step": pms, "GFLOP": pfl / 1e9,
-                                      "TFLOP/s": pfl / (pms * 1e-3) / 1e12, "calls": len(steps_)}
+                                      "TFLOP/s": pfl / (pms * 1e-3) / 1e12, "calls": len(steps_),
+                                      "step": us_stats(t_pair)}
     out["ring_pairs_128k"] = pair_rows
     del kfull, vfull, qfull
     # backward (and forward + backward) on the 8K slice and on one 8K sequence
@@ -190,13 +233,14 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
         cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
         o, lse = ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale)
         dq, dk, dv = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
-        _, fwd_ms = timed_launches(lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse),
-                                   steps // 4, warmup, torch)
-        _, bwd_ms = timed_launches(lambda: ops.hdp_attn_varlen_bwd(qq, kk, vv, o, lse, dd, cu, w.scale,
-                                                                   dq=dq, dk=dk, dv=dv), steps // 4, warmup, torch)
+        t_f = timed_floor(lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse), torch)
+        t_b = timed_floor(lambda: ops.hdp_attn_varlen_bwd(qq, kk, vv, o, lse, dd, cu, w.scale,
+                                                          dq=dq, dk=dk, dv=dv), torch)
+        fwd_ms, bwd_ms = t_f["mean_ms"], t_b["mean_ms"]
         ff = sum(ops.hdp_seq_flops(s, w.H, w.D, True, 0) for s in w.lengths)
         fb = sum(ops.hdp_seq_flops(s, w.H, w.D, True, 1) for s in w.lengths)
         out[w.name] = {"fwd_us": fwd_ms * 1e3, "bwd_us": bwd_ms * 1e3,
+                       "fwd": us_stats(t_f), "bwd": us_stats(t_b),
                        "fwd_TFLOP/s": ff / (fwd_ms * 1e-3) / 1e12,
                        "bwd_TFLOP/s": fb / (bwd_ms * 1e-3) / 1e12,
                        "fwd_bwd_TFLOP/s": (ff + fb) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12}
@@ -207,11 +251,11 @@ def detail_rows(torch, ops, synth, steps: int, warmup: int):
         cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
         o = torch.empty_like(qq)
         lse = torch.empty((qq.shape[0], w.H), dtype=torch.float32, device="cuda")
-        _, ms = timed_launches(lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse),
-                               steps // 4, warmup, torch)
+        t_m = timed_floor(lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse), torch)
+        ms = t_m["mean_ms"]
         fl = sum(ops.hdp_seq_flops(s, w.H, w.D) for s in w.lengths)
         out[w.name] = {"n_seq": len(w.lengths), "GFLOP": fl / 1e9, "kernel_us": ms * 1e3,
-                       "TFLOP/s": fl / (ms * 1e-3) / 1e12}
+                       "TFLOP/s": fl / (ms * 1e-3) / 1e12, "launch": us_stats(t_m)}
     # every throughput also as a fraction of its roofline: TFLOP/s against the bf16 MFMA peak,
     # GB/s against HBM
     def add_fracs(row):
@@ -232,6 +276,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed launches of the headline step before its warm-up, so the timed "
+                         "steps run at the steady clock")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -269,9 +316,16 @@ def main() -> int:
     def step():
         ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale, out=out, lse=lse)
 
-    ms_step, ms_kernel = timed_launches(step, args.steps, args.warmup, torch)
+    clock = settle_clock(step, torch, args.settle_ms)
+    t = timed_launches(step, args.steps, args.warmup, torch)
+    ms_step, ms_kernel = t["ms_step"], t["mean_ms"]
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
+    mhz = ops.hdp_probe_clock()
+    clock["mfma_clock_mhz_after"] = round(mhz, 1)
+    clock["note"] = ("untimed launches of the same step for settle_ms before the warm-up steps, so that "
+                     "the timed steps run at the steady clock; mfma_clock_mhz_after is the shader clock "
+                     "measured right after the timed steps under back-to-back MFMAs on every CU")
     result = {
         "metric": "varlen attn TFLOP/s on 8K-token packed slice; % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -291,10 +345,14 @@ def main() -> int:
                    "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(), "kernel_us": round(ms_kernel * 1e3, 2)},
+                     "traffic": load_traffic(), "kernel_us": round(ms_kernel * 1e3, 2),
+                     "launch": us_stats(t),
+                     "peak_at_measured_clock": round(PEAK_BF16_TFLOPS * mhz / NOMINAL_MHZ, 1),
+                     "frac_at_measured_clock": round(achieved / (PEAK_BF16_TFLOPS * mhz / NOMINAL_MHZ), 4)},
+        "clock": clock,
     }
     if not args.no_detail:
-        result["detail"] = detail_rows(torch, ops, synth, args.steps, args.warmup)
+        result["detail"] = detail_rows(torch, ops, synth)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, cu)
     print(json.dumps(result), flush=True)

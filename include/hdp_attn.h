@@ -32,12 +32,19 @@
  *     outside rows 0 .. cu[n_seq]-1.  Rows outside [cu[0], cu[n_seq]) are left untouched.
  *   - Supported head dims: D = 64 and D = 128 (else HDP_ERR_UNSUPPORTED); head counts
  *     H <= 65535 (else HDP_ERR_OVERFLOW).
- *   - The library owns one small workspace per device (work-queue counters and, for the
- *     backward, every row's lse and delta as fp32, 2 x rows x H), grown on demand.  Calls that
- *     overlap in time on one device (different streams or host threads) share it and must not
- *     run concurrently.  hdp_release_workspace() frees it.  For tests of the error path, a
- *     set environment variable HDP_TEST_FAIL_ALLOC makes every growth of the workspace fail
- *     (HDP_ERR_HIP, nothing launched).
+ *   - The library owns a small state per (device, stream): work-queue counters and, for the
+ *     backward, every row's lse and delta as fp32 (2 x rows x H), grown on demand.  It is
+ *     allocated stream-ordered (hipMallocAsync / hipFreeAsync on the call's stream, no
+ *     device-wide synchronisation), so calls on different streams never share it and may run
+ *     concurrently; calls on one stream are ordered by the stream.  The state is keyed by the
+ *     stream handle: destroy a stream only after its calls have completed.
+ *     hdp_release_workspace() frees the current device's state (it synchronises the device).
+ *     For tests of the error path, a set environment variable HDP_TEST_FAIL_ALLOC makes every
+ *     growth of the backward workspace fail (HDP_ERR_HIP, nothing launched).
+ *   - With the environment variable HDP_VALIDATE set, the calls that take cu_seqlens copy it to
+ *     the host first (synchronising the stream) and return HDP_ERR_INVALID_ARG unless cu[0] = 0,
+ *     the entries do not decrease and (backward) cu[n_seq] <= T.  A debugging aid, off by
+ *     default: the hot path never waits on the host.
  */
 #ifndef HDP_ATTN_H
 #define HDP_ATTN_H
@@ -112,8 +119,9 @@ int hdp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float
  *     dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * out)),  dQ = scale dS K,  dK = scale dS^T Q,
  * dK and dV summed over the H/Hkv query heads of each key/value head.
  *   q, k, v, out, dout bf16 as in the forward; lse fp32 [T][H] from the forward.
- *   T: total packed tokens (the caller's row count, = cu[n_seq]); sizes the fp32 workspace and
- *   bounds every access (sequences are clamped to rows 0 .. T-1).
+ *   T: total packed tokens (the caller's row count, = cu[n_seq]).  Not in the forward's list:
+ *   the backward needs it on the host, without reading cu_seqlens from the device, to size its
+ *   fp32 workspace before the launch; the kernels also clamp every sequence to rows 0 .. T-1.
  *   dq [T][H][D], dk, dv [T][Hkv][D] bf16 (written).
  */
 int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -203,6 +211,15 @@ int hdp_plan_unit_flops(const int64_t* lens, int32_t n_seq, int32_t n_units,
  */
 int hdp_plan_balance(const uint64_t* cost, const int32_t* unit_ring, int32_t n_units,
                      int32_t n_ranks, uint64_t delta, int32_t* unit_rank, uint64_t* rank_load);
+
+/*
+ * Measurement helper, not part of the attention path: the shader clock (MHz) the current device
+ * sustains while every CU issues back-to-back bf16 MFMAs for `iters` iterations (shader-clock
+ * counter cycles over the constant 100 MHz real-time counter's elapsed time).  Roofline
+ * fractions are quoted against the nominal 2.4 GHz and against this clock.  Allocates a few
+ * bytes stream-ordered and synchronises `stream` to read the result into *mhz.
+ */
+int hdp_probe_clock(int32_t iters, double* mhz, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* hdp_status_string(int status);

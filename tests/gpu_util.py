@@ -50,6 +50,25 @@ def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
     return np.where(a > 0, 2.0 ** (e - 8), 0.0)
 
 
+def fp32_close(gpu_t, ref: np.ndarray, tol: float = TOL_BF16_OUT) -> float:
+    """Plain max-abs check of an fp32 result (no rounding slack: nothing is rounded to bf16)."""
+    g = gpu_t.detach().float().cpu().double().numpy()
+    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
+    assert err <= tol, err
+    return err
+
+
+def boundary_rows(n: int, stride: int = 8, extra=()):
+    """Every stride-th row of 0..n-1, the rows on either side of every 64-row and 128-row tile
+    edge, the first and last row, and any extra rows (sorted, unique)."""
+    rows = set(range(0, n, stride))
+    for e in range(0, n + 1, 64):
+        rows.update((e - 1, e))
+    rows.update((0, n - 1))
+    rows.update(int(x) for x in extra)
+    return np.array(sorted(r for r in rows if 0 <= r < n), dtype=np.int64)
+
+
 def grad_close(gpu_t, ref: np.ndarray, tol: float = TOL_BF16_OUT, mean_tol: float = 2e-3):
     """bf16 gradient check: |gpu - ref| <= tol + half a bf16 ulp of ref everywhere, and the mean
     error stays small.  Returns (max error, max error beyond the half ulp, mean error)."""

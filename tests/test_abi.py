@@ -160,3 +160,11 @@ def test_other_entry_points_validate_before_touching_the_gpu():
               NULL, None) == _lib.HDP_OK
     for st in range(5):
         assert _lib.lib().hdp_status_string(st).startswith(b"HDP_")
+
+
+def test_clock_probe_validates_before_any_hip_call():
+    lib = _lib.lib()
+    import ctypes
+    mhz = ctypes.c_double(0.0)
+    assert lib.hdp_probe_clock(0, ctypes.addressof(mhz), None) == _lib.HDP_ERR_INVALID_ARG
+    assert lib.hdp_probe_clock(100, None, None) == _lib.HDP_ERR_INVALID_ARG

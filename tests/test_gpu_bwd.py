@@ -6,16 +6,15 @@ value at best; gradient magnitudes reach 8-16 here, where that half ulp (0.03) a
 value, and the mean error must stay below 2e-3.
 
 The GPU backward consumes the GPU forward's out and lse (as a training step would); the oracle
-differentiates its own fp64 forward.  Small packs compare every element of dq, dk and dv; the
-full-size workloads compare sampled rows the oracle evaluates one by one (dq rows anywhere,
-dk/dv rows where the rows that see them are few enough to evaluate).
+differentiates its own fp64 forward.  Every case compares every element of dq, dk and dv, the
+full-size ones included (the 8K packed slice and one whole 8192-token sequence).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import grad_close, to_gpu
+from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, grad_close, max_abs, to_gpu
 from variable_length_attention_amd import ops, synth
 
 pytestmark = pytest.mark.gpu
@@ -107,36 +106,27 @@ def test_backward_is_deterministic_and_isolated_per_sequence():
         assert torch.equal(x[keep].view(torch.int16), y[keep].view(torch.int16))
 
 
-def tail_key_rows(cu, per_seq=(0, 1, 7, 63, 200), long_cut=1200):
-    """Key rows whose gradient needs few rows: near each sequence's end, plus the first key of
-    the shorter sequences."""
-    rows = set()
-    for i in range(len(cu) - 1):
-        a, b = int(cu[i]), int(cu[i + 1])
-        for d in per_seq:
-            if b - 1 - d >= a:
-                rows.add(b - 1 - d)
-        if 0 < b - a <= long_cut:
-            rows.add(a)
-    return np.array(sorted(rows), dtype=np.int64)
-
-
 @pytest.mark.parametrize("make", [synth.fwd_bwd_8k_slice, synth.fwd_bwd_8k_single])
-def test_backward_full_size_sampled(make):
+def test_forward_backward_full_size_every_row(make):
+    # Both 8K slices of the forward + backward workload (the packed slice and one whole 8192-token
+    # sequence): every row and head of out, lse, dq and every key row of dk, dv against the
+    # oracle, including the first key tiles of the longest sequences, which collect the most rows.
     w = make()
     q, k, v, do = synth.varlen_tensors(w, with_dout=True)
     cu = synth.cu_seqlens(w.lengths)
-    dq, dk, dv = run_fwd_bwd(w, q, k, v, do, cu)
-    T = int(cu[-1])
-    qrows = np.unique(np.concatenate([np.arange(0, T, 97), cu[:-1], cu[1:] - 1]))
-    qrows = qrows[(qrows >= 0) & (qrows < T)]
-    krows = tail_key_rows(cu)
-    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, w.scale, qrows=qrows, krows=krows)
-    iq = torch.from_numpy(qrows).cuda()
-    ik = torch.from_numpy(krows).cuda()
-    for name, g, r in (("dq", dq[iq], rq), ("dk", dk[ik], rk), ("dv", dv[ik], rv)):
+    qg, kg, vg, dog = to_gpu(q, k, v, do)
+    cug = torch.from_numpy(cu).cuda()
+    out, lse = ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale)
+    dq, dk, dv = ops.hdp_attn_varlen_bwd(qg, kg, vg, out, lse, dog, cug, w.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print("%s forward: all %d rows, max|dout|=%.3g max|dlse|=%.3g" % (w.name, int(cu[-1]), e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+    del ro, rl
+    rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, w.scale)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         e = grad_close(g, r)
-        print("%s %s (%d dq rows, %d dk/dv rows): max %.3g, beyond half-ulp %.3g, mean %.2g"
-              % (w.name, name, len(qrows), len(krows), *e))
+        print("%s %s (every row): max %.3g, beyond half-ulp %.3g, mean %.2g" % (w.name, name, *e))
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()

@@ -3,8 +3,8 @@
 Each case hands the same inputs to both sides: bf16 q/k/v/out/dO and fp32 lse (for the small
 cases, the oracle's own forward of the slice over its chunks, rounded; at full size, the seeded
 synthetic out/lse of synth.ring_bwd_tensors).  The GPU adds its result to fp32 accumulators,
-which start at zero unless stated.  Tolerance as for the packed backward (the products run on
-bf16 P and dS): |gpu - oracle| <= 2e-2 + half a bf16 ulp of the oracle value, mean <= 2e-3.
+which start at zero unless stated.  Those accumulators are never rounded to bf16, so the check
+is a plain max-abs 2e-2 on every compared element.
 """
 import math
 
@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import grad_close
+from gpu_util import boundary_rows, fp32_close
 from variable_length_attention_amd import ops, synth
 
 pytestmark = pytest.mark.gpu
@@ -63,9 +63,8 @@ def test_chunk_backward_small_full(Lq, Lk, q_off, kv_off, causal, H, Hkv, D):
     dq, dk, dv = run_gpu(q, k, v, q_off, kv_off, causal, scale, out, lse, do)
     rq, rk, rv = oracle.chunk_bwd(q, k, v, q_off, kv_off, causal, scale, out, lse, do)
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        e = grad_close(g, r)
-        print("Lq=%d Lk=%d q_off=%d kv_off=%d causal=%d %s: max %.3g beyond half-ulp %.3g mean %.2g"
-              % (Lq, Lk, q_off, kv_off, causal, name, *e))
+        e = fp32_close(g, r)
+        print("Lq=%d Lk=%d q_off=%d kv_off=%d causal=%d %s: max %.3g" % (Lq, Lk, q_off, kv_off, causal, name, e))
 
 
 def test_future_chunk_adds_nothing_and_accumulators_are_updated_in_place():
@@ -97,7 +96,7 @@ def test_future_chunk_adds_nothing_and_accumulators_are_updated_in_place():
     dq, dk, dv = run_gpu(q, k2, v2, q_off, 200, True, 0.1, out2, lse2, do, init=init)
     rq, rk, rv = oracle.chunk_bwd(q, k2, v2, q_off, 200, True, 0.1, out2, lse2, do)
     for g, r, i in ((dq, rq, init[0]), (dk, rk, init[1]), (dv, rv, init[2])):
-        grad_close(g.cpu() - i, r)
+        fp32_close(g.cpu() - i, r)
 
 
 def test_rows_that_see_no_key_contribute_nothing():
@@ -116,7 +115,7 @@ def test_rows_that_see_no_key_contribute_nothing():
     rq, rk, rv = oracle.chunk_bwd(q, k, v, 0, 40, True, 0.1, out, lse, do)
     for g, r in ((dq, rq), (dk, rk), (dv, rv)):
         assert torch.isfinite(g).all()
-        grad_close(g.cpu(), r)
+        fp32_close(g.cpu(), r)
     assert (dq[:40] == 0).all()
 
 
@@ -142,7 +141,7 @@ def test_ring_of_chunks_sums_to_the_packed_backward():
     torch.cuda.synchronize()
     rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, scale)
     for g, r in ((dq, rq), (dk, rk), (dv, rv)):
-        grad_close(g, r)
+        fp32_close(g, r)
 
 
 @pytest.mark.parametrize("chunk", [15, 0, 14])
@@ -156,13 +155,14 @@ def test_chunk_backward_full_size_sampled(chunk):
     c0 = chunk * w.chunk_len
     kc, vc = k[c0:c0 + w.chunk_len], v[c0:c0 + w.chunk_len]
     dq, dk, dv = run_gpu(q, kc, vc, w.q_offset, c0, True, scale, out, lse, do)
-    qrows = np.unique(np.concatenate([np.arange(0, w.q_len, 331), [w.q_len - 1]])).astype(np.int64)
-    krows = np.unique(np.concatenate([np.arange(0, w.chunk_len, 401), [w.chunk_len - 1]])).astype(np.int64)
+    # every 32nd row, both sides of every 64-row tile edge and the last row
+    qrows = boundary_rows(w.q_len, 32)
+    krows = boundary_rows(w.chunk_len, 32)
     rq, rk, rv = oracle.chunk_bwd(q, kc, vc, w.q_offset, c0, True, scale, out, lse, do,
                                   qrows=qrows, krows=krows)
     iq, ik = torch.from_numpy(qrows).cuda(), torch.from_numpy(krows).cuda()
     for name, g, r in (("dq", dq[iq], rq), ("dk", dk[ik], rk), ("dv", dv[ik], rv)):
-        e = grad_close(g, r)
-        print("chunk %d %s (%d rows): max %.3g beyond half-ulp %.3g mean %.2g" % (chunk, name, len(r), *e))
+        e = fp32_close(g, r)
+        print("chunk %d %s (%d rows): max %.3g" % (chunk, name, len(r), e))
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()

@@ -1,8 +1,8 @@
 """GPU parity of the forward paths against the fp64 oracle, through the C ABI.
 
-Small cases compare every element; the full-size workloads compare a deterministic row sample
-(every 8th/16th/64th packed row plus the first and last row of every sequence, all heads) that
-the oracle evaluates row by row.  Exactness properties of the packing (a query attends only to
+Small cases and the 8K packed slice compare every element; the 32K micro-batches and the ring
+share compare a deterministic row sample (every 8th row, both sides of every tile edge and the
+first and last row of every sequence, all heads) that the oracle evaluates row by row.  Exactness properties of the packing (a query attends only to
 its own sequence) are checked bit for bit.
 """
 import math
@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, TOL_F32, lse_close, max_abs, sample_rows, to_gpu
+from gpu_util import (TOL_BF16_LSE, TOL_BF16_OUT, TOL_F32, boundary_rows, lse_close, max_abs,
+                      sample_rows, to_gpu)
 from variable_length_attention_amd import ops, synth
 
 pytestmark = pytest.mark.gpu
@@ -60,15 +61,28 @@ def test_bf16_ragged_pack_full(H, Hkv, D):
     assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
 
 
-@pytest.mark.parametrize("make,stride", [(synth.packed_slice_8k, 8),
-                                         (synth.microbatch_32k_short, 16),
-                                         (synth.microbatch_32k_long, 64)])
-def test_full_size_workloads_sampled(make, stride):
+def test_packed_slice_8k_every_row():
+    # One rank's whole 8192-token slice (9 sequences): every row and head against the oracle.
+    # This is the digest's §3.1-§3.2 rule in full: each packed sequence attends only to itself.
+    w = synth.packed_slice_8k()
+    q, k, v = synth.varlen_tensors(w)
+    cu = synth.cu_seqlens(w.lengths)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print("%s: all %d rows, max|dout|=%.3g max|dlse|=%.3g" % (w.name, int(cu[-1]), e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+
+
+@pytest.mark.parametrize("make", [synth.microbatch_32k_short, synth.microbatch_32k_long])
+def test_microbatch_32k_sampled(make):
+    # Every 8th packed row, both sides of every 64-row tile edge and the first and last row of
+    # every sequence, all heads.
     w = make()
     q, k, v = synth.varlen_tensors(w)
     cu = synth.cu_seqlens(w.lengths)
     out, lse = run_fwd(q, k, v, cu, w.scale)
-    rows = sample_rows(cu, stride)
+    rows = np.union1d(sample_rows(cu, 8), boundary_rows(int(cu[-1]), 8))
     ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale, rows=rows)
     idx = torch.from_numpy(rows).cuda()
     e_out = max_abs(out[idx], ro)
@@ -221,7 +235,8 @@ def test_ring_128k_share_merged_equals_full_causal_attention_sampled():
         ops.hdp_lse_merge(acc_o, acc_l, part_o, part_l,
                           out_bf16=out_bf16 if c == w.n_chunks - 1 else None)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, w.q_len, 512), [1, 2, 4095, 4096, w.q_len - 1]]))
+    # every 8th row and both sides of every 64-row tile edge of the slice, all heads
+    rows = boundary_rows(w.q_len, 8, extra=(1, 2))
     idx = torch.from_numpy(rows).cuda()
     ro, rl = oracle.chunk_partial(q, k, v, w.q_offset, 0, True, w.scale, rows=rows)
     e_o = max_abs(acc_o[idx], ro)

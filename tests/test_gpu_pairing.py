@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, grad_close, lse_close, max_abs
+from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, fp32_close, lse_close, max_abs
 from variable_length_attention_amd import ops, synth
 
 pytestmark = pytest.mark.gpu
@@ -79,4 +79,4 @@ def test_paired_ring_backward_sums_to_the_packed_backward():
     torch.cuda.synchronize()
     rq, rk, rv = oracle.varlen_bwd(q, k, v, do, cu, scale)
     for g, r in ((dq, rq), (dk, rk), (dv, rv)):
-        grad_close(g, r)
+        fp32_close(g, r)

@@ -62,7 +62,17 @@ def test_pair_chunks_validation():
     assert L.hdp_pair_chunks(10, 0, 0, pa, pb) == _lib.HDP_ERR_INVALID_ARG
     assert L.hdp_pair_chunks(10, 4, 4, pa, pb) == _lib.HDP_ERR_INVALID_ARG
     assert L.hdp_pair_chunks(10, 4, 1, None, pb) == _lib.HDP_ERR_INVALID_ARG
-    assert L.hdp_pair_chunks(1 << 60, 4, 1, pa, pb) == _lib.HDP_ERR_OVERFLOW
+
+
+@pytest.mark.parametrize("s,N,k", [(1 << 60, 4, 1), ((1 << 63) - 1, 2 ** 31 - 1, 2 ** 31 - 2),
+                                   ((1 << 62) + 12345, 2 ** 30 + 7, 5), (10 ** 18, 3, 2)])
+def test_pair_chunks_bounds_exact_at_int64_limits(s, N, k):
+    # c * s exceeds 64 bits here: the bounds floor(c s / 2N) must still be exact
+    (o0, l0), (o1, l1) = ops.hdp_pair_chunks(s, N, k)
+    n2 = 2 * N
+    assert (o0, l0) == (k * s // n2, (k + 1) * s // n2 - k * s // n2)
+    c = n2 - 1 - k
+    assert (o1, l1) == (c * s // n2, (c + 1) * s // n2 - c * s // n2)
 
 
 # ---------------------------------------------------------------------- HDP sharding

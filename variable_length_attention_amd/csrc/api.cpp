@@ -4,8 +4,9 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
-#include <unordered_map>
+#include <vector>
 
 #include "hdp_attn.h"
 #include "hdp_internal.h"
@@ -14,55 +15,84 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct DeviceState {
-    int cus = 0;
+// Library state is kept per (device, stream): each stream has its own work-queue counters and
+// its own backward workspace, so calls that run concurrently on different streams of one device
+// never share them.  Everything is allocated stream-ordered on the stream of the call that first
+// needs it (no device-wide synchronisation); the counters are cleared by a fill kernel on that
+// stream, and the kernels leave them at zero when they finish.
+struct StreamState {
     int* counters = nullptr;   // hdp::kCounterInts ints, zero between launches
-    void* ws = nullptr;        // backward workspace
+    void* ws = nullptr;        // backward workspace (lse in log2 units and delta, per row and head)
     size_t ws_bytes = 0;
 };
 
-std::mutex g_mu;
-std::unordered_map<int, DeviceState> g_dev;
+struct DeviceState {
+    int cus = 0;
+    std::map<hipStream_t, StreamState> streams;
+};
 
-// Returns the calling thread's current device state, creating the counters on first use.
-int device_state(DeviceState** out) {
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+
+// The calling thread's current device and the state of `stream` on it, created on first use.
+int stream_state(hipStream_t stream, int* cus, StreamState** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return HDP_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_mu);
-    DeviceState& st = g_dev[dev];
-    if (st.counters == nullptr) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    DeviceState& ds = g_dev[dev];
+    if (ds.cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             return HDP_ERR_HIP;
+        ds.cus = n;
+    }
+    StreamState& st = ds.streams[stream];
+    if (st.counters == nullptr) {
         int* c = nullptr;
-        if (hipMalloc(&c, sizeof(int) * hdp::kCounterInts) != hipSuccess) return HDP_ERR_HIP;
-        if (hipMemset(c, 0, sizeof(int) * hdp::kCounterInts) != hipSuccess ||
-            hipDeviceSynchronize() != hipSuccess) {
-            (void)hipFree(c);
+        if (hipMallocAsync((void**)&c, sizeof(int) * hdp::kCounterInts, stream) != hipSuccess) return HDP_ERR_HIP;
+        if (hdp::launch_fill_zero(c, hdp::kCounterInts, stream) != hipSuccess) {
+            (void)hipFreeAsync(c, stream);
             return HDP_ERR_HIP;
         }
-        st.cus = cus;
         st.counters = c;
     }
+    *cus = ds.cus;
     *out = &st;
     return HDP_OK;
 }
 
-// Grows the backward workspace to at least `bytes` (synchronises the device when it grows).
-int ensure_workspace(DeviceState* st, size_t bytes) {
+// Grows a stream's backward workspace to at least `bytes`, stream-ordered: the old buffer is
+// released after the work already queued on the stream and the new one is ready before the
+// work queued next.  A set HDP_TEST_FAIL_ALLOC makes every growth fail (error-path tests).
+int ensure_workspace(StreamState* st, size_t bytes, hipStream_t stream) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (st->ws_bytes >= bytes) return HDP_OK;
     if (std::getenv("HDP_TEST_FAIL_ALLOC") != nullptr) return HDP_ERR_HIP;
     if (st->ws != nullptr) {
-        if (hipDeviceSynchronize() != hipSuccess) return HDP_ERR_HIP;
-        (void)hipFree(st->ws);
+        if (hipFreeAsync(st->ws, stream) != hipSuccess) return HDP_ERR_HIP;
         st->ws = nullptr;
         st->ws_bytes = 0;
     }
     void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) return HDP_ERR_HIP;
+    if (hipMallocAsync(&p, bytes, stream) != hipSuccess) return HDP_ERR_HIP;
     st->ws = p;
     st->ws_bytes = bytes;
+    return HDP_OK;
+}
+
+// Optional host-side check of cu_seqlens (a set HDP_VALIDATE): copies it to the host, which
+// synchronises the stream, and requires cu[0] = 0, non-decreasing entries and cu[n] <= T
+// (T < 0: no bound).  Off by default: the hot path never waits on the host.
+int validate_cu(const int32_t* cu, int32_t n_seq, int64_t T, hipStream_t stream) {
+    if (std::getenv("HDP_VALIDATE") == nullptr) return HDP_OK;
+    std::vector<int32_t> h((size_t)n_seq + 1);
+    if (hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return HDP_ERR_HIP;
+    if (h[0] != 0) return HDP_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n_seq; ++i)
+        if (h[i + 1] < h[i]) return HDP_ERR_INVALID_ARG;
+    if (T >= 0 && h[n_seq] > T) return HDP_ERR_INVALID_ARG;
     return HDP_OK;
 }
 
@@ -83,9 +113,9 @@ int heads_per_item(int32_t H, int32_t Hkv) {
     return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
-void schedule(const DeviceState* st, int32_t H, int32_t Hkv, hdp::FwdArgs& a, int& grid) {
+void schedule(int cus, const StreamState* st, int32_t H, int32_t Hkv, hdp::FwdArgs& a, int& grid) {
     a.hpw = heads_per_item(H, Hkv);
-    grid = st->cus;
+    grid = cus;
     const int nhb = H / a.hpw;
     a.nqueues = (nhb % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0) ? hdp::kMaxQueues : 1;
     a.counters = st->counters;
@@ -165,8 +195,10 @@ int hdp_attn_varlen_fwd(const void* q, const void* k, const void* v, const int32
     if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
     if (n_seq == 0) return HDP_OK;
     if (!q || !k || !v || !cu_seqlens || !out || !lse) return HDP_ERR_INVALID_ARG;
-    DeviceState* st = nullptr;
-    if (int rc = device_state(&st)) return rc;
+    if (int rc = validate_cu(cu_seqlens, n_seq, -1, stream)) return rc;
+    int cus = 0;
+    StreamState* st = nullptr;
+    if (int rc = stream_state(stream, &cus, &st)) return rc;
     hdp::FwdArgs a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -180,7 +212,7 @@ int hdp_attn_varlen_fwd(const void* q, const void* k, const void* v, const int32
     a.lse = lse;
     a.causal = 1;
     int grid = 0;
-    schedule(st, H, Hkv, a, grid);
+    schedule(cus, st, H, Hkv, a, grid);
     return hdp::launch_fwd_varlen(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 
@@ -193,6 +225,7 @@ int hdp_attn_varlen_fwd_f32(const float* q, const float* k, const float* v,
     if (n_seq == 0) return HDP_OK;
     if (!q || !k || !v || !cu_seqlens || !out || !lse) return HDP_ERR_INVALID_ARG;
     if (H > 65535) return HDP_ERR_OVERFLOW;
+    if (int rc = validate_cu(cu_seqlens, n_seq, -1, stream)) return rc;
     hdp::F32Args a{};
     a.q = q;
     a.k = k;
@@ -220,8 +253,9 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
     if (Lq == 0) return HDP_OK;
     if (!q_slice || !o_partial || !lse) return HDP_ERR_INVALID_ARG;
     if (Lk > 0 && (!k_chunk || !v_chunk)) return HDP_ERR_INVALID_ARG;
-    DeviceState* st = nullptr;
-    if (int rc = device_state(&st)) return rc;
+    int cus = 0;
+    StreamState* st = nullptr;
+    if (int rc = stream_state(stream, &cus, &st)) return rc;
     hdp::FwdArgs a{};
     a.q = (const uint16_t*)q_slice;
     a.k = (const uint16_t*)k_chunk;
@@ -239,7 +273,7 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
     a.delta = (int32_t)std::max<int64_t>(-(int64_t)Lq, std::min<int64_t>(d, Lk));
     a.causal = causal ? 1 : 0;
     int grid = 0;
-    schedule(st, H, Hkv, a, grid);
+    schedule(cus, st, H, Hkv, a, grid);
     return hdp::launch_fwd_chunk(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 
@@ -273,9 +307,11 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     if (!q || !k || !v || !out || !lse || !dout || !cu_seqlens || !dq || !dk || !dv)
         return HDP_ERR_INVALID_ARG;
     if ((int64_t)T * H > (int64_t)INT32_MAX) return HDP_ERR_OVERFLOW;
-    DeviceState* st = nullptr;
-    if (int rc = device_state(&st)) return rc;
-    if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)T * (size_t)H)) return rc;
+    if (int rc = validate_cu(cu_seqlens, n_seq, T, stream)) return rc;
+    int cus = 0;
+    StreamState* st = nullptr;
+    if (int rc = stream_state(stream, &cus, &st)) return rc;
+    if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)T * (size_t)H, stream)) return rc;
     hdp::BwdArgs a{};
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k;
@@ -296,7 +332,7 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
     a.dv = (uint16_t*)dv;
     a.counters = st->counters;
     a.hpw = heads_per_item(H, Hkv);
-    const int grid = st->cus;
+    const int grid = cus;
     const bool q8 = (H / a.hpw) % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
     const bool kv8 = Hkv % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
     a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
@@ -318,9 +354,10 @@ int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, con
     if (Lq == 0 || Lk == 0) return HDP_OK;
     if (!q_slice || !k_chunk || !v_chunk || !out || !lse || !dout || !dq_acc || !dk_acc || !dv_acc)
         return HDP_ERR_INVALID_ARG;
-    DeviceState* st = nullptr;
-    if (int rc = device_state(&st)) return rc;
-    if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)Lq * (size_t)H)) return rc;
+    int cus = 0;
+    StreamState* st = nullptr;
+    if (int rc = stream_state(stream, &cus, &st)) return rc;
+    if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)Lq * (size_t)H, stream)) return rc;
     hdp::BwdArgs a{};
     a.q = (const uint16_t*)q_slice;
     a.k = (const uint16_t*)k_chunk;
@@ -345,7 +382,7 @@ int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, con
     a.dv_acc = dv_acc;
     a.counters = st->counters;
     a.hpw = heads_per_item(H, Hkv);
-    const int grid = st->cus;
+    const int grid = cus;
     const bool q8 = (H / a.hpw) % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
     const bool kv8 = Hkv % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
     a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
@@ -359,11 +396,16 @@ int hdp_release_workspace(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     auto itr = g_dev.find(dev);
     if (itr == g_dev.end()) return HDP_OK;
+    // every stream's queued work ends before its memory goes back
     if (hipDeviceSynchronize() != hipSuccess) return HDP_ERR_HIP;
-    if (itr->second.ws) (void)hipFree(itr->second.ws);
-    if (itr->second.counters) (void)hipFree(itr->second.counters);
+    int rc = HDP_OK;
+    for (auto& kv : itr->second.streams) {
+        if (kv.second.ws && hipFreeAsync(kv.second.ws, nullptr) != hipSuccess) rc = HDP_ERR_HIP;
+        if (kv.second.counters && hipFreeAsync(kv.second.counters, nullptr) != hipSuccess) rc = HDP_ERR_HIP;
+    }
     g_dev.erase(itr);
-    return HDP_OK;
+    if (hipDeviceSynchronize() != hipSuccess) rc = HDP_ERR_HIP;
+    return rc;
 }
 
 }  // extern "C"

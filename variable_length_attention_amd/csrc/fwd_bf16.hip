@@ -632,6 +632,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // earlier would hand out the queue's large items before it is known which workgroup
         // finishes first.  The atomic's latency passes under the output stores.
         if (wave == 0) k_next = pop();
+        // Waves 2-3 staged their query rows in the output tiles, and the first workgroup barrier
+        // after read_q is the stage turn of unit 1: an item of a single unit has none, so one
+        // is taken here before any wave overwrites a tile that another may still be reading.
+        if (n_units == 1) __syncthreads();
         store_rows(o, m, l);
         if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
         __syncthreads();

@@ -94,6 +94,9 @@ hipError_t launch_fwd_varlen(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_chunk(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+// Writes n zero ints at p with a kernel (not a memset node, so the call may be recorded into a
+// graph that is replayed).
+hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs& a, int D, int grid, hipStream_t s);
 

@@ -53,7 +53,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     }
 }
 
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(int* p, int n) {
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_fill_zero(int* p, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int blocks = (n + kThreads - 1) / kThreads < 64 ? (n + kThreads - 1) / kThreads : 64;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, s, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
     const int tpr = a.D / 4;

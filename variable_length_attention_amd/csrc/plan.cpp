@@ -16,9 +16,10 @@ extern "C" {
 int hdp_pair_chunks(int64_t s, int32_t n_ranks, int32_t rank, int64_t* offsets, int64_t* lengths) {
     if (s < 0 || n_ranks <= 0 || rank < 0 || rank >= n_ranks || !offsets || !lengths)
         return HDP_ERR_INVALID_ARG;
-    if (s > (INT64_MAX >> 21)) return HDP_ERR_OVERFLOW;    // c * s below fits in int64
     const int64_t n2 = 2 * (int64_t)n_ranks;
-    auto bound = [&](int64_t c) { return c * s / n2; };    // chunk c = [bound(c), bound(c+1))
+    // chunk c = [bound(c), bound(c+1)); c <= 2N and s < 2^63, so c * s fits in 128 bits and the
+    // quotient, at most s, fits in int64
+    auto bound = [&](int64_t c) { return (int64_t)((__int128)c * s / n2); };
     const int64_t c[2] = {rank, n2 - 1 - rank};
     for (int i = 0; i < 2; ++i) {
         offsets[i] = bound(c[i]);
@@ -67,7 +68,7 @@ extern "C" int hdp_plan_shard(const int64_t* lens, int32_t n_seq, int64_t C, int
                 if (int st = hdp_pair_chunks(s, (int32_t)N, (int32_t)r, off, len)) return st;
                 for (int h = 0; h < 2; ++h) { u.seqs.push_back(i); u.span.push_back({off[h], len[h]}); }
             } else {
-                const int64_t a = r * s / N, b = (r + 1) * s / N;
+                const int64_t a = (int64_t)((__int128)r * s / N), b = (int64_t)((__int128)(r + 1) * s / N);
                 u.seqs.push_back(i);
                 u.span.push_back({a, b - a});
             }

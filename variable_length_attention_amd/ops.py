@@ -37,6 +37,20 @@ def _dev_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int) -> No
         raise ValueError("%s must be contiguous" % name)
 
 
+def _shapes(fn: str, **named) -> None:
+    """Every tensor must have exactly the shape the kernels index it with: a smaller or
+    mis-shaped buffer would be read or written out of bounds on the device."""
+    for name, (t, want) in named.items():
+        if tuple(t.shape) != tuple(int(x) for x in want):
+            raise ValueError("%s: %s has shape %s, expected %s" % (fn, name, tuple(t.shape), tuple(want)))
+
+
+def _same_device(fn: str, *ts) -> None:
+    devs = set(t.device for t in ts if t is not None)
+    if len(devs) > 1:
+        raise ValueError("%s: tensors on different devices %s" % (fn, sorted(map(str, devs))))
+
+
 def _scale(D: int, scale: Optional[float]) -> float:
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
@@ -55,6 +69,9 @@ def hdp_attn_varlen_fwd(q, k, v, cu_seqlens, scale=None, out=None, lse=None
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _dev_tensor("out", out, torch.bfloat16, 3)
     _dev_tensor("lse", lse, torch.float32, 2)
+    _shapes("hdp_attn_varlen_fwd", k=(k, (T, Hkv, D)), v=(v, (T, Hkv, D)), out=(out, (T, H, D)),
+            lse=(lse, (T, H)))
+    _same_device("hdp_attn_varlen_fwd", q, k, v, cu_seqlens, out, lse)
     st = _lib.lib().hdp_attn_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
                                         cu_seqlens.numel() - 1, H, Hkv, D, _scale(D, scale),
                                         _ptr(out), _ptr(lse), _stream())
@@ -76,6 +93,9 @@ def hdp_attn_varlen_fwd_f32(q, k, v, cu_seqlens, scale=None, out=None, lse=None
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     _dev_tensor("out", out, torch.float32, 3)
     _dev_tensor("lse", lse, torch.float32, 2)
+    _shapes("hdp_attn_varlen_fwd_f32", k=(k, (T, Hkv, D)), v=(v, (T, Hkv, D)),
+            out=(out, (T, H, D)), lse=(lse, (T, H)))
+    _same_device("hdp_attn_varlen_fwd_f32", q, k, v, cu_seqlens, out, lse)
     st = _lib.lib().hdp_attn_varlen_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens),
                                             cu_seqlens.numel() - 1, H, Hkv, D, _scale(D, scale),
                                             _ptr(out), _ptr(lse), _stream())
@@ -97,6 +117,9 @@ def hdp_attn_chunk_partial(q_slice, k_chunk, v_chunk, q_offset: int, kv_offset: 
         lse = torch.empty((Lq, H), dtype=torch.float32, device=q_slice.device)
     _dev_tensor("o_partial", o_partial, torch.float32, 3)
     _dev_tensor("lse", lse, torch.float32, 2)
+    _shapes("hdp_attn_chunk_partial", v_chunk=(v_chunk, (Lk, Hkv, D)), k_chunk=(k_chunk, (Lk, Hkv, D)),
+            o_partial=(o_partial, (Lq, H, D)), lse=(lse, (Lq, H)))
+    _same_device("hdp_attn_chunk_partial", q_slice, k_chunk, v_chunk, o_partial, lse)
     st = _lib.lib().hdp_attn_chunk_partial(_ptr(q_slice), Lq, _ptr(k_chunk), _ptr(v_chunk), Lk,
                                            int(q_offset), int(kv_offset), int(bool(causal)), H,
                                            Hkv, D, _scale(D, scale), _ptr(o_partial), _ptr(lse),
@@ -114,6 +137,10 @@ def hdp_lse_merge(o_acc, lse_acc, o_part, lse_part, out_bf16=None) -> None:
     L, H, D = o_acc.shape
     if out_bf16 is not None:
         _dev_tensor("out_bf16", out_bf16, torch.bfloat16, 3)
+        _shapes("hdp_lse_merge", out_bf16=(out_bf16, (L, H, D)))
+    _shapes("hdp_lse_merge", lse_acc=(lse_acc, (L, H)), o_part=(o_part, (L, H, D)),
+            lse_part=(lse_part, (L, H)))
+    _same_device("hdp_lse_merge", o_acc, lse_acc, o_part, lse_part, out_bf16)
     st = _lib.lib().hdp_lse_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), L, H,
                                   D, _ptr(out_bf16), _stream())
     _lib.check("hdp_lse_merge", st)
@@ -133,6 +160,10 @@ def hdp_attn_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, scale=None, dq=None
     dv = torch.empty_like(v) if dv is None else dv
     for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _dev_tensor(n, t, torch.bfloat16, 3)
+    _shapes("hdp_attn_varlen_bwd", k=(k, (T, Hkv, D)), v=(v, (T, Hkv, D)), out=(out, (T, H, D)),
+            lse=(lse, (T, H)), dout=(dout, (T, H, D)), dq=(dq, (T, H, D)), dk=(dk, (T, Hkv, D)),
+            dv=(dv, (T, Hkv, D)))
+    _same_device("hdp_attn_varlen_bwd", q, k, v, out, lse, dout, cu_seqlens, dq, dk, dv)
     st = _lib.lib().hdp_attn_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                         _ptr(dout), _ptr(cu_seqlens), cu_seqlens.numel() - 1, T,
                                         H, Hkv, D, _scale(D, scale), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -153,10 +184,10 @@ def hdp_attn_chunk_bwd(q_slice, k_chunk, v_chunk, q_offset: int, kv_offset: int,
         _dev_tensor(n, t, torch.float32, 3)
     Lq, H, D = q_slice.shape
     Lk, Hkv = k_chunk.shape[0], k_chunk.shape[1]
-    if (tuple(out.shape) != (Lq, H, D) or tuple(dout.shape) != (Lq, H, D) or tuple(lse.shape) != (Lq, H)
-            or tuple(dq_acc.shape) != (Lq, H, D) or tuple(v_chunk.shape) != (Lk, Hkv, D)
-            or tuple(dk_acc.shape) != (Lk, Hkv, D) or tuple(dv_acc.shape) != (Lk, Hkv, D)):
-        raise ValueError("hdp_attn_chunk_bwd: inconsistent shapes")
+    _shapes("hdp_attn_chunk_bwd", k_chunk=(k_chunk, (Lk, Hkv, D)), v_chunk=(v_chunk, (Lk, Hkv, D)),
+            out=(out, (Lq, H, D)), dout=(dout, (Lq, H, D)), lse=(lse, (Lq, H)),
+            dq_acc=(dq_acc, (Lq, H, D)), dk_acc=(dk_acc, (Lk, Hkv, D)), dv_acc=(dv_acc, (Lk, Hkv, D)))
+    _same_device("hdp_attn_chunk_bwd", q_slice, k_chunk, v_chunk, out, lse, dout, dq_acc, dk_acc, dv_acc)
     st = _lib.lib().hdp_attn_chunk_bwd(_ptr(q_slice), Lq, _ptr(k_chunk), _ptr(v_chunk), Lk,
                                        int(q_offset), int(kv_offset), int(bool(causal)), H, Hkv, D,
                                        _scale(D, scale), _ptr(out), _ptr(lse), _ptr(dout),
@@ -253,6 +284,13 @@ def hdp_plan_balance(cost, unit_ring, n_ranks: int, delta: int = 0):
                                      int(delta), ctypes.addressof(ur), ctypes.addressof(load))
     _lib.check("hdp_plan_balance", st)
     return [int(x) for x in ur][:U], [int(x) for x in load]
+
+
+def hdp_probe_clock(iters: int = 20000) -> float:
+    """Shader clock (MHz) sustained under back-to-back MFMAs on every CU (measurement helper)."""
+    mhz = ctypes.c_double(0.0)
+    _lib.check("hdp_probe_clock", _lib.lib().hdp_probe_clock(int(iters), ctypes.addressof(mhz), _stream()))
+    return float(mhz.value)
 
 
 def hdp_release_workspace() -> None:
