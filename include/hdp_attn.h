@@ -61,7 +61,8 @@ typedef enum {
     HDP_ERR_INVALID_ARG = 1, /* null pointer with work to do, bad sizes, H % Hkv != 0, ... */
     HDP_ERR_UNSUPPORTED = 2, /* head dim other than 64 / 128 */
     HDP_ERR_HIP = 3,         /* a HIP launch or allocation failed */
-    HDP_ERR_OVERFLOW = 4     /* a size product does not fit the index types */
+    HDP_ERR_OVERFLOW = 4,    /* a size product does not fit the index types */
+    HDP_ERR_SCRATCH_LIMIT = 5 /* larger than the fixed scratch of hdp_attn_varlen_bwd_noalloc */
 } hdp_status_t;
 
 enum { HDP_PASS_FWD = 0, HDP_PASS_BWD = 1, HDP_PASS_FWD_BWD = 2 };
@@ -128,6 +129,24 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
                         const float* lse, const void* dout, const int32_t* cu_seqlens,
                         int32_t n_seq, int32_t T, int32_t H, int32_t Hkv, int32_t D,
                         float scale, void* dq, void* dk, void* dv, hipStream_t stream);
+
+/*
+ * hdp_attn_varlen_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or training loops, harnesses that forbid allocation.  Same arguments,
+ * kernels and results (bit for bit) as hdp_attn_varlen_bwd, but the library allocates nothing:
+ * its scratch (work-queue counters and 2 x T x H fp32 row values) lives in one fixed device array
+ * of HDP_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  Sizes need
+ * 4096 + 8 * T * H <= HDP_NOALLOC_SCRATCH_BYTES (T * H <= 2,096,640, e.g. T <= 65,520 at H = 32),
+ * else HDP_ERR_SCRATCH_LIMIT and nothing is launched.  The counters are cleared by a kernel at
+ * the start of every call.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (two streams, two host threads) race and give wrong results; serialise them.
+ * HDP_VALIDATE is not honoured here (it would copy to the host).
+ */
+#define HDP_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+int hdp_attn_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                const float* lse, const void* dout, const int32_t* cu_seqlens,
+                                int32_t n_seq, int32_t T, int32_t H, int32_t Hkv, int32_t D,
+                                float scale, void* dq, void* dk, void* dv, hipStream_t stream);
 
 /*
  * Backward of one ring step (the counterpart of hdp_attn_chunk_partial): the slice's rows

@@ -168,3 +168,19 @@ def test_clock_probe_validates_before_any_hip_call():
     mhz = ctypes.c_double(0.0)
     assert lib.hdp_probe_clock(0, ctypes.addressof(mhz), None) == _lib.HDP_ERR_INVALID_ARG
     assert lib.hdp_probe_clock(100, None, None) == _lib.HDP_ERR_INVALID_ARG
+
+
+def test_noalloc_backward_rejects_sizes_beyond_its_scratch_before_any_hip_call():
+    # 4096 + 8 * T * H must fit the fixed scratch; the check comes before any HIP call, so the
+    # (never dereferenced) pointers here are placeholders
+    lib = _lib.lib()
+    p = 4096
+    limit = (_lib.NOALLOC_SCRATCH_BYTES - 4096) // 8          # largest T * H
+    H = 32
+    T = limit // H + 1
+    st = lib.hdp_attn_varlen_bwd_noalloc(p, p, p, p, p, p, p, 1, T, H, 8, 128, 0.1, p, p, p, None)
+    assert st == _lib.HDP_ERR_SCRATCH_LIMIT
+    assert b"no-allocation" in lib.hdp_status_string(st)
+    # invalid arguments are reported as for the allocating entry point
+    assert lib.hdp_attn_varlen_bwd_noalloc(p, p, p, p, p, p, p, 1, 10, 6, 4, 128, 0.1, p, p, p, None) == _lib.HDP_ERR_INVALID_ARG
+    assert lib.hdp_attn_varlen_bwd_noalloc(p, p, p, p, p, p, p, 0, 10, 8, 2, 128, 0.1, p, p, p, None) == _lib.HDP_OK

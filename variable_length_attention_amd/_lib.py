@@ -15,6 +15,8 @@ HDP_ERR_INVALID_ARG = 1
 HDP_ERR_UNSUPPORTED = 2
 HDP_ERR_HIP = 3
 HDP_ERR_OVERFLOW = 4
+HDP_ERR_SCRATCH_LIMIT = 5
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 # (name, restype, argtypes) for every symbol include/hdp_attn.h declares.
 P, I32, I64, F32, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64
@@ -24,6 +26,7 @@ SIGNATURES = {
     "hdp_attn_chunk_partial": (I32, [P, I32, P, P, I32, I64, I64, I32, I32, I32, I32, F32, P, P, P]),
     "hdp_lse_merge": (I32, [P, P, P, P, I32, I32, I32, P, P]),
     "hdp_attn_varlen_bwd": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, P]),
+    "hdp_attn_varlen_bwd_noalloc": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, P]),
     "hdp_attn_chunk_bwd": (I32, [P, I32, P, P, I32, I64, I64, I32, I32, I32, I32, F32, P, P, P, P, P,
                                  P, P]),
     "hdp_seq_flops": (U64, [I64, I32, I32, I32, I32]),

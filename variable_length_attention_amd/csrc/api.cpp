@@ -150,6 +150,55 @@ uint64_t flops_from_pairs(unsigned __int128 pairs, int32_t H, int32_t D, int32_t
 
 }  // namespace
 
+namespace hdp {
+
+int check_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, const int32_t* cu_seqlens, int32_t n_seq, int32_t T, int32_t H,
+                     int32_t Hkv, int32_t D, float scale, const void* dq, const void* dk, const void* dv) {
+    if (n_seq < 0 || T < 0) return HDP_ERR_INVALID_ARG;
+    if (int st = check_heads(H, Hkv, D)) return st;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (n_seq == 0 || T == 0) return HDP_OK;
+    if (!q || !k || !v || !out || !lse || !dout || !cu_seqlens || !dq || !dk || !dv)
+        return HDP_ERR_INVALID_ARG;
+    if ((int64_t)T * H > (int64_t)INT32_MAX) return HDP_ERR_OVERFLOW;
+    return HDP_OK;
+}
+
+int launch_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, const int32_t* cu_seqlens, int32_t n_seq, int32_t T, int32_t H,
+                      int32_t Hkv, int32_t D, float scale, void* dq, void* dk, void* dv, int* counters,
+                      float* rowvals, int cus, hipStream_t stream) {
+    BwdArgs a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.out = (const uint16_t*)out;
+    a.lse = lse;
+    a.dout = (const uint16_t*)dout;
+    a.cu = cu_seqlens;
+    a.n_seq = n_seq;
+    a.T = T;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.scale = scale;
+    a.scale_log2 = scale * kLog2e;
+    a.rowvals = rowvals;
+    a.dq = (uint16_t*)dq;
+    a.dk = (uint16_t*)dk;
+    a.dv = (uint16_t*)dv;
+    a.counters = counters;
+    a.hpw = heads_per_item(H, Hkv);
+    const int grid = cus;
+    const bool q8 = (H / a.hpw) % kMaxQueues == 0 && grid % kMaxQueues == 0;
+    const bool kv8 = Hkv % kMaxQueues == 0 && grid % kMaxQueues == 0;
+    a.nqueues_q = q8 ? kMaxQueues : 1;
+    a.nqueues_kv = kv8 ? kMaxQueues : 1;
+    return launch_bwd(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+}  // namespace hdp
+
 extern "C" {
 
 const char* hdp_status_string(int status) {
@@ -159,6 +208,9 @@ const char* hdp_status_string(int status) {
         case HDP_ERR_UNSUPPORTED: return "HDP_ERR_UNSUPPORTED: unsupported head dim (64 or 128)";
         case HDP_ERR_HIP: return "HDP_ERR_HIP: HIP launch or allocation failed";
         case HDP_ERR_OVERFLOW: return "HDP_ERR_OVERFLOW: size does not fit the index types";
+        case HDP_ERR_SCRATCH_LIMIT:
+            return "HDP_ERR_SCRATCH_LIMIT: 4096 + 8*T*H bytes exceed the fixed scratch of the "
+                   "no-allocation entry point (HDP_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown hdp status";
     }
 }
@@ -300,44 +352,16 @@ int hdp_attn_varlen_bwd(const void* q, const void* k, const void* v, const void*
                         const float* lse, const void* dout, const int32_t* cu_seqlens,
                         int32_t n_seq, int32_t T, int32_t H, int32_t Hkv, int32_t D,
                         float scale, void* dq, void* dk, void* dv, hipStream_t stream) {
-    if (n_seq < 0 || T < 0) return HDP_ERR_INVALID_ARG;
-    if (int st = check_heads(H, Hkv, D)) return st;
-    if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
+    if (int rc = hdp::check_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, n_seq, T, H, Hkv, D, scale, dq, dk, dv))
+        return rc;
     if (n_seq == 0 || T == 0) return HDP_OK;
-    if (!q || !k || !v || !out || !lse || !dout || !cu_seqlens || !dq || !dk || !dv)
-        return HDP_ERR_INVALID_ARG;
-    if ((int64_t)T * H > (int64_t)INT32_MAX) return HDP_ERR_OVERFLOW;
     if (int rc = validate_cu(cu_seqlens, n_seq, T, stream)) return rc;
     int cus = 0;
     StreamState* st = nullptr;
     if (int rc = stream_state(stream, &cus, &st)) return rc;
     if (int rc = ensure_workspace(st, 2 * sizeof(float) * (size_t)T * (size_t)H, stream)) return rc;
-    hdp::BwdArgs a{};
-    a.q = (const uint16_t*)q;
-    a.k = (const uint16_t*)k;
-    a.v = (const uint16_t*)v;
-    a.out = (const uint16_t*)out;
-    a.lse = lse;
-    a.dout = (const uint16_t*)dout;
-    a.cu = cu_seqlens;
-    a.n_seq = n_seq;
-    a.T = T;
-    a.H = H;
-    a.Hkv = Hkv;
-    a.scale = scale;
-    a.scale_log2 = scale * kLog2e;
-    a.rowvals = (float*)st->ws;
-    a.dq = (uint16_t*)dq;
-    a.dk = (uint16_t*)dk;
-    a.dv = (uint16_t*)dv;
-    a.counters = st->counters;
-    a.hpw = heads_per_item(H, Hkv);
-    const int grid = cus;
-    const bool q8 = (H / a.hpw) % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
-    const bool kv8 = Hkv % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
-    a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
-    a.nqueues_kv = kv8 ? hdp::kMaxQueues : 1;
-    return hdp::launch_bwd(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+    return hdp::launch_varlen_bwd(q, k, v, out, lse, dout, cu_seqlens, n_seq, T, H, Hkv, D, scale, dq, dk, dv,
+                                  st->counters, (float*)st->ws, cus, stream);
 }
 
 int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, const void* v_chunk,

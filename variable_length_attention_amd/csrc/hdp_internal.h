@@ -98,6 +98,18 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 // graph that is replayed).
 hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int D, int grid, hipStream_t s);
+
+// The packed backward's host side, shared by the entry point that owns its workspace and the
+// one that uses a fixed scratch: argument checks (a status; HDP_OK also for the no-op sizes),
+// then the two launches with the given queue counters (zero on entry) and row-value workspace
+// (2 * T * H floats).
+int check_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                     const void* dout, const int32_t* cu_seqlens, int32_t n_seq, int32_t T, int32_t H,
+                     int32_t Hkv, int32_t D, float scale, const void* dq, const void* dk, const void* dv);
+int launch_varlen_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                      const void* dout, const int32_t* cu_seqlens, int32_t n_seq, int32_t T, int32_t H,
+                      int32_t Hkv, int32_t D, float scale, void* dq, void* dk, void* dv, int* counters,
+                      float* rowvals, int cus, hipStream_t stream);
 hipError_t launch_bwd_chunk(const BwdArgs& a, int D, int grid, hipStream_t s);
 
 }  // namespace hdp
