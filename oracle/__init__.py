@@ -43,8 +43,11 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    build()
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("HDP_ORACLE_LIB_PATH")   # another build of this file (sanitizers)
+    if not path:
+        build()
+        path = _LIB
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.orc_varlen_fwd.argtypes = [P, P, P, P, i64, i32, i32, i32, f64, P, i64, P, P, i32]

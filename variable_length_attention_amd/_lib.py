@@ -8,7 +8,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhdpattn.so")
+# HDP_LIB_PATH selects another build of the same library (the sanitizer build of the host layer)
+LIB_PATH = os.environ.get("HDP_LIB_PATH") or os.path.join(_PKG, "libhdpattn.so")
 
 HDP_OK = 0
 HDP_ERR_INVALID_ARG = 1
