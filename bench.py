@@ -271,6 +271,92 @@ def detail_rows(torch, ops, synth):
     return out
 
 
+def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
+    """Per-workgroup busy time of the forward on the 8K slice and both 32K micro-batches: the
+    persistent kernel runs one workgroup per CU, each records when it started and when it finished
+    its last item (hdp_set_trace).  Reported per workload, averaged over `launches` launches:
+    finish time of the last / mean / first workgroup after the first one started, in us, and the
+    last workgroup of each XCD (workgroup w runs on XCD w mod 8)."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    trace = torch.zeros(4 * n_cu, dtype=torch.int64, device="cuda")
+    out = {}
+    for make in (synth.packed_slice_8k, synth.microbatch_32k_long, synth.microbatch_32k_short):
+        w = make()
+        qq, kk, vv = (t.cuda() for t in synth.varlen_tensors(w))
+        cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
+        o = torch.empty_like(qq)
+        lse = torch.empty((qq.shape[0], w.H), dtype=torch.float32, device="cuda")
+
+        def step():
+            ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse)
+
+        settle_clock(step, torch, 300.0)
+        rows = []
+        ops.hdp_set_trace(trace)
+        try:
+            for _ in range(launches):
+                trace.zero_()
+                step()
+                torch.cuda.synchronize()
+                t = trace.view(n_cu, 4).cpu().numpy()
+                rows.append(t.copy())
+        finally:
+            ops.hdp_set_trace(None)
+        fin, busy, items, xcd_last = [], [], [], []
+        for t in rows:
+            t0 = int(t[:, 0].min())
+            f = (t[:, 1] - t0) / 100.0            # 100 MHz real-time counter -> us
+            fin.append(f)
+            busy.append((t[:, 1] - t[:, 0]) / 100.0)
+            items.append(t[:, 2])
+            xcd_last.append([float(f[x::8].max()) for x in range(8)])
+        import numpy as np
+        fin, busy, items = np.array(fin), np.array(busy), np.array(items)
+        out[w.name] = {
+            "n_seq": len(w.lengths), "launches": launches, "workgroups": n_cu,
+            "last_finish_us": round(float(fin.max(axis=1).mean()), 2),
+            "mean_finish_us": round(float(fin.mean(axis=1).mean()), 2),
+            "first_finish_us": round(float(fin.min(axis=1).mean()), 2),
+            "mean_busy_us": round(float(busy.mean()), 2),
+            "busy_over_last_finish": round(float(busy.mean(axis=1).mean() / fin.max(axis=1).mean()), 4),
+            "items_per_workgroup_min_mean_max": [int(items.min()), round(float(items.mean()), 2), int(items.max())],
+            "xcd_last_finish_us": [round(float(x), 2) for x in np.array(xcd_last).mean(axis=0)],
+        }
+        del qq, kk, vv, o, lse
+    return out
+
+
+def run_sample(torch, ops, synth, name: str, launches: int) -> dict:
+    """`launches` launches of one named workload with nothing else around them: the command a
+    counter profile of one kernel runs (slice_fwd, long_fwd, short_fwd, ring_chunk, merge,
+    slice_bwd, single_bwd)."""
+    if name in ("ring_chunk", "merge"):
+        w = synth.ring_chunks_128k()
+        q, k, v = (t.cuda() for t in synth.ring_tensors(w))
+        L = w.chunk_len
+        po, pl = ops.hdp_attn_chunk_partial(q, k[:L], v[:L], w.q_offset, 0, True, w.scale)
+        acc_o, acc_l = po.clone(), pl.clone()
+        if name == "ring_chunk":
+            fn = lambda: ops.hdp_attn_chunk_partial(q, k[:L], v[:L], w.q_offset, 0, True, w.scale, o_partial=po, lse=pl)
+        else:
+            fn = lambda: ops.hdp_lse_merge(acc_o, acc_l, po, pl)
+    else:
+        make = {"slice_fwd": synth.packed_slice_8k, "long_fwd": synth.microbatch_32k_long,
+                "short_fwd": synth.microbatch_32k_short, "slice_bwd": synth.fwd_bwd_8k_slice,
+                "single_bwd": synth.fwd_bwd_8k_single}[name]
+        w = make()
+        qq, kk, vv, dd = (t.cuda() for t in synth.varlen_tensors(w, with_dout=True))
+        cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
+        o, lse = ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale)
+        if name.endswith("_fwd"):
+            fn = lambda: ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse)
+        else:
+            dq, dk, dv = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+            fn = lambda: ops.hdp_attn_varlen_bwd(qq, kk, vv, o, lse, dd, cu, w.scale, dq=dq, dk=dk, dv=dv)
+    t = timed_launches(fn, launches, 2, torch)
+    return {"sample": name, **us_stats(t)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +367,12 @@ def main() -> int:
                          "steps run at the steady clock")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sample", default=None,
+                    help="only time --steps launches of one workload (slice_fwd, long_fwd, short_fwd, "
+                         "ring_chunk, merge, slice_bwd, single_bwd), for counter profiles")
+    ap.add_argument("--cu-timeline", action="store_true",
+                    help="print only the per-workgroup (one per CU) finish-time summary of the forward "
+                         "on the 8K slice and the 32K micro-batches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy 512 MiB device-to-device 3 times (a known-size kernel that "
                          "calibrates the HBM byte counters of a profiler run)")
@@ -296,6 +388,9 @@ def main() -> int:
     from variable_length_attention_amd import ops, synth
 
     torch.cuda.set_device(0)
+    if args.cu_timeline:
+        print(json.dumps({"cu_timeline": cu_timeline(torch, ops, synth)}), flush=True)
+        return 0
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -304,6 +399,9 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.sample:
+        print(json.dumps(run_sample(torch, ops, synth, args.sample, args.steps)), flush=True)
+        return 0
     w = synth.packed_slice_8k()
     q, k, v = synth.varlen_tensors(w)
     cu = synth.cu_seqlens(w.lengths)

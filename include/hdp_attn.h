@@ -240,6 +240,17 @@ int hdp_plan_balance(const uint64_t* cost, const int32_t* unit_ring, int32_t n_u
  */
 int hdp_probe_clock(int32_t iters, double* mhz, hipStream_t stream);
 
+/*
+ * Measurement helper, not part of the attention path: per-workgroup trace of the forward
+ * kernel (hdp_attn_varlen_fwd, hdp_attn_chunk_partial).  With trace != NULL (device memory of
+ * 4 x capacity int64) every later forward launch whose persistent grid (one workgroup per CU)
+ * fits the capacity writes, for workgroup w: trace[4w] = the real-time counter (100 MHz) when
+ * it started, trace[4w+1] = when it finished its last item, trace[4w+2] = items it processed,
+ * trace[4w+3] = 0.  The buffer is overwritten by each such launch.  capacity 0 turns it off.
+ * This is how the FLOP-ordered scheduling's balance across CUs is measured.
+ */
+int hdp_set_trace(long long* trace, int32_t capacity);
+
 /* Static text for a status code. */
 const char* hdp_status_string(int status);
 

@@ -1,6 +1,7 @@
 // C ABI of the per-rank attention library: argument checks, per-device workspace, FLOP cost
 // model and kernel launches.  Every check happens on the host before any HIP call.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -113,12 +114,17 @@ int heads_per_item(int32_t H, int32_t Hkv) {
     return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
+// Forward workgroup trace (measurement helper): a device buffer and its capacity in workgroups.
+std::atomic<long long*> g_trace{nullptr};
+std::atomic<int> g_trace_cap{0};
+
 void schedule(int cus, const StreamState* st, int32_t H, int32_t Hkv, hdp::FwdArgs& a, int& grid) {
     a.hpw = heads_per_item(H, Hkv);
     grid = cus;
     const int nhb = H / a.hpw;
     a.nqueues = (nhb % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0) ? hdp::kMaxQueues : 1;
     a.counters = st->counters;
+    a.trace = g_trace_cap.load() >= grid ? g_trace.load() : nullptr;
 }
 
 // sum_{r=0}^{n-1} clamp(a + r, 0, cap), exactly.
@@ -412,6 +418,14 @@ int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, con
     a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
     a.nqueues_kv = kv8 ? hdp::kMaxQueues : 1;
     return hdp::launch_bwd_chunk(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+int hdp_set_trace(long long* trace, int32_t capacity) {
+    if (capacity < 0 || (capacity > 0 && trace == nullptr)) return HDP_ERR_INVALID_ARG;
+    g_trace_cap.store(0);
+    g_trace.store(capacity > 0 ? trace : nullptr);
+    g_trace_cap.store(capacity);
+    return HDP_OK;
 }
 
 int hdp_release_workspace(void) {

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
+    if (args.trace != nullptr && tid == 0) args.trace[(int64_t)blockIdx.x * kTraceWords] = (long long)__builtin_amdgcn_s_memrealtime();
 
     const int H = args.H, Hkv = args.Hkv;
     const int G = H / Hkv;
@@ -178,7 +179,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     if (wave == 0) publish(__shfl(pop(), 0), 0);
     __syncthreads();
 
-    for (int it = 0;; ++it) {
+    int it = 0;                                  // items processed
+    for (;; ++it) {
         const int slot = it & 1;
         int k_next = 0;
         // item fields are uniform: keep them in scalar registers
@@ -641,7 +643,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         __syncthreads();
     }
 
-    if (tid == 0) queue_finish(args.counters);
+    if (tid == 0) {
+        if (args.trace != nullptr) {
+            long long* t = args.trace + (int64_t)blockIdx.x * kTraceWords;
+            t[1] = (long long)__builtin_amdgcn_s_memrealtime();
+            t[2] = it;
+            t[3] = 0;
+        }
+        queue_finish(args.counters);
+    }
 }
 
 }  // namespace

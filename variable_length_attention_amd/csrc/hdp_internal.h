@@ -33,7 +33,12 @@ struct FwdArgs {
     int* counters;          // kCounterInts ints, zero on entry
     int32_t hpw;            // query heads per workgroup item (1, 2 or 4)
     int32_t nqueues;        // 8 (one per XCD) or 1
+    // measurement: null, or kTraceWords words per workgroup (real-time counter at start and
+    // end, items processed, unused)
+    long long* trace;
 };
+
+constexpr int kTraceWords = 4;
 
 struct F32Args {
     const float* q;

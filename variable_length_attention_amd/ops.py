@@ -293,5 +293,15 @@ def hdp_probe_clock(iters: int = 20000) -> float:
     return float(mhz.value)
 
 
+def hdp_set_trace(trace: Optional[torch.Tensor]) -> None:
+    """Per-workgroup forward trace into an int64 device tensor of 4 words per workgroup (None:
+    off).  Measurement helper."""
+    if trace is None:
+        _lib.check("hdp_set_trace", _lib.lib().hdp_set_trace(None, 0))
+        return
+    _dev_tensor("trace", trace, torch.int64, 1)
+    _lib.check("hdp_set_trace", _lib.lib().hdp_set_trace(trace.data_ptr(), trace.numel() // 4))
+
+
 def hdp_release_workspace() -> None:
     _lib.check("hdp_release_workspace", _lib.lib().hdp_release_workspace())
