@@ -135,7 +135,7 @@ def cpu_baseline(w, q, k, v, cu):
 def detail_rows(torch, ops, synth):
     """Other rows of the hot path, timed the same way (context, not the headline)."""
     out = {}
-    # ring-chunk share: 16 chunk partials + 15 LSE merges
+    # ring-chunk share: 16 chunk partials + 15 LSE merges (and the same with the merge fused)
     w = synth.ring_chunks_128k()
     q, k, v = (t.cuda() for t in synth.ring_tensors(w))
     L = w.chunk_len
@@ -155,6 +155,13 @@ def detail_rows(torch, ops, synth):
     t_ring = timed_floor(ring_step, torch)
     ms = t_ring["ms_step"]
     fl = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D) for c in range(w.n_chunks))
+    # the same share with each step's merge fused into its epilogue (hdp_attn_chunk_merge)
+    def ring_step_fused():
+        acc_l.fill_(-float("inf"))
+        for c in range(w.n_chunks):
+            ops.hdp_attn_chunk_merge(q, chunks[c][0], chunks[c][1], w.q_offset, c * L, acc_o, acc_l, True, w.scale)
+
+    t_fused = timed_floor(ring_step_fused, torch)
     t_merge = timed_floor(lambda: ops.hdp_lse_merge(acc_o, acc_l, po, pl), torch, min_launches=200)
     merge_ms = t_merge["mean_ms"]
     merge_bytes = w.q_len * w.H * (12 * w.D + 12)
@@ -177,6 +184,9 @@ def detail_rows(torch, ops, synth):
     fb = sum(ops.hdp_chunk_flops(w.q_len, L, w.q_offset, c * L, True, w.H, w.D, 1) for c in range(w.n_chunks))
     out["ring_chunks_128k"] = {"ms_per_step": ms, "TFLOP/s": fl / (ms * 1e-3) / 1e12,
                                "step": us_stats(t_ring),
+                               "fused_ms_per_step": t_fused["ms_step"],
+                               "fused_TFLOP/s": fl / (t_fused["ms_step"] * 1e-3) / 1e12,
+                               "fused_step": us_stats(t_fused),
                                "merge_us": merge_ms * 1e3,
                                "merge_GB/s": merge_bytes / (merge_ms * 1e-3) / 1e9,
                                "merge": us_stats(t_merge),

@@ -102,6 +102,24 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
                            float* o_partial, float* lse, hipStream_t stream);
 
 /*
+ * One ring step with its merge fused (digest §3.2: each step computes on the chunk in hand and
+ * the steps' results are combined): the same attention of the slice against the chunk as
+ * hdp_attn_chunk_partial, merged by log-sum-exp into the running result in place, as
+ * hdp_lse_merge would do with that partial, without writing the partial out:
+ *   o_acc [Lq][H][D], lse_acc [Lq][H] fp32: read and overwritten.  A row whose lse_acc is -inf
+ *   has seen no key yet: its o_acc is ignored (it may hold anything).  A row that sees no key of
+ *   this chunk keeps its values (and keeps o_acc = 0 if it has seen none at all).
+ *   out_bf16: NULL, or [Lq][H][D] bf16 that receives the merged o_acc rounded to bf16.
+ * Start a ring with lse_acc = -inf (any o_acc) or with the first step's hdp_attn_chunk_partial.
+ * HBM traffic of the merge: 1,032 bytes per (row, head) at D = 128 against 2,064 for a partial
+ * written out and merged by hdp_lse_merge.  Other arguments as hdp_attn_chunk_partial.
+ */
+int hdp_attn_chunk_merge(const void* q_slice, int32_t Lq, const void* k_chunk, const void* v_chunk,
+                         int32_t Lk, int64_t q_offset, int64_t kv_offset, int32_t causal, int32_t H,
+                         int32_t Hkv, int32_t D, float scale, float* o_acc, float* lse_acc,
+                         void* out_bf16, hipStream_t stream);
+
+/*
  * Log-sum-exp merge of two partials over disjoint key sets, in place (the ring's per-step
  * combination, digest §3.2).  For each of the L*H (token, head) rows:
  *     m = max(l_acc, l_part); w = exp(l - m); o_acc = (w_acc o_acc + w_part o_part)/(w_acc + w_part);

@@ -276,3 +276,94 @@ def test_lse_merge_matches_oracle_including_empty_partials(D):
     ref_bf = torch.from_numpy(ro).float().to(torch.bfloat16).double().numpy()
     assert max_abs(bf, ref_bf) <= TOL_BF16_OUT
     assert not torch.isnan(go).any()
+
+
+# ------------------------------------------------------------------ fused ring step
+
+
+def ring_reference(q, k, v, q_off, pieces, causal, scale, rows=None):
+    """The oracle's merge of the pieces' partials in ring order (fp64)."""
+    acc_o = acc_l = None
+    for ko, kl in pieces:
+        o, l = oracle.chunk_partial(q, k[ko:ko + kl], v[ko:ko + kl], q_off, ko, causal, scale, rows=rows)
+        if acc_o is None:
+            acc_o, acc_l = o, l
+        else:
+            acc_o, acc_l = oracle.lse_merge(acc_o, acc_l, o, l)
+    return acc_o, acc_l
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("Lq,q_off,pieces,causal", [
+    (200, 300, [(0, 192), (192, 150), (342, 64)], True),    # past, diagonal-crossing, future-ish chunks
+    (130, 0, [(0, 70), (70, 70), (500, 30)], True),         # rows with no key in some chunks, one empty chunk
+    (77, 1000, [(0, 33), (33, 129)], False),                # no mask
+    (64, 64, [(64, 64), (0, 64), (128, 0)], True),          # tile-exact, out of order, empty chunk
+])
+def test_chunk_merge_equals_partials_merged_by_the_oracle(Lq, q_off, pieces, causal, D):
+    # The fused ring step merges each chunk's partial into the running result; starting from
+    # lse_acc = -inf with garbage (NaN) in o_acc, the result must equal the oracle's partials
+    # merged in the same order, and the bf16 copy must be that result rounded.
+    H, Hkv = 8, 2
+    rng = np.random.default_rng(170 + Lq)
+    S = max(o + l for o, l in pieces)
+    q = synth.normal(rng, (Lq, H, D), "bf16")
+    k = synth.normal(rng, (S, Hkv, D), "bf16")
+    v = synth.normal(rng, (S, Hkv, D), "bf16")
+    scale = 1 / math.sqrt(D)
+    qg, kg, vg = to_gpu(q, k, v)
+    o_acc = torch.full((Lq, H, D), float("nan"), device="cuda")
+    l_acc = torch.full((Lq, H), -float("inf"), device="cuda")
+    ob = torch.empty((Lq, H, D), dtype=torch.bfloat16, device="cuda")
+    for i, (ko, kl) in enumerate(pieces):
+        ops.hdp_attn_chunk_merge(qg, kg[ko:ko + kl], vg[ko:ko + kl], q_off, ko, o_acc, l_acc, causal, scale,
+                                 out_bf16=ob if i == len(pieces) - 1 else None)
+    torch.cuda.synchronize()
+    ro, rl = ring_reference(q, k, v, q_off, pieces, causal, scale)
+    # rows that saw no key at all: 0 and -inf
+    ro = np.where(np.isneginf(rl)[:, :, None], 0.0, ro)
+    assert max_abs(o_acc, ro) <= TOL_BF16_OUT
+    lse_close(l_acc, rl, TOL_BF16_LSE)
+    assert max_abs(ob, ro) <= TOL_BF16_OUT
+    assert torch.equal(ob.view(torch.int16), o_acc.to(torch.bfloat16).view(torch.int16))
+
+
+def test_chunk_merge_agrees_with_partial_then_merge():
+    # Fused and unfused ring steps compute the same merge in a different arithmetic order.
+    H, Hkv, D, Lq = 32, 8, 128, 300
+    rng = np.random.default_rng(180)
+    q = synth.normal(rng, (Lq, H, D), "bf16").cuda()
+    k = synth.normal(rng, (900, Hkv, D), "bf16").cuda()
+    v = synth.normal(rng, (900, Hkv, D), "bf16").cuda()
+    scale = 1 / math.sqrt(D)
+    pieces = [(0, 300), (300, 300), (600, 300)]
+    a_o, a_l = ops.hdp_attn_chunk_partial(q, k[:300], v[:300], 600, 0, True, scale)
+    b_o, b_l = a_o.clone(), a_l.clone()
+    for ko, kl in pieces[1:]:
+        po, pl = ops.hdp_attn_chunk_partial(q, k[ko:ko + kl], v[ko:ko + kl], 600, ko, True, scale)
+        ops.hdp_lse_merge(a_o, a_l, po, pl)
+        ops.hdp_attn_chunk_merge(q, k[ko:ko + kl], v[ko:ko + kl], 600, ko, b_o, b_l, True, scale)
+    torch.cuda.synchronize()
+    assert float((a_o - b_o).abs().max()) <= 1e-5
+    assert float((a_l - b_l).abs().max()) <= 1e-5
+
+
+def test_ring_128k_share_fused_merge_equals_full_causal_attention_sampled():
+    # The ring share of the 128K sequence as 16 fused steps from an empty accumulator.
+    w = synth.ring_chunks_128k()
+    q, k, v = synth.ring_tensors(w)
+    qg, kg, vg = to_gpu(q, k, v)
+    L = w.chunk_len
+    o_acc = torch.zeros((w.q_len, w.H, w.D), device="cuda")
+    l_acc = torch.full((w.q_len, w.H), -float("inf"), device="cuda")
+    ob = torch.empty((w.q_len, w.H, w.D), dtype=torch.bfloat16, device="cuda")
+    for c in range(w.n_chunks):
+        ops.hdp_attn_chunk_merge(qg, kg[c * L:(c + 1) * L], vg[c * L:(c + 1) * L], w.q_offset, c * L, o_acc, l_acc,
+                                 True, w.scale, out_bf16=ob if c == w.n_chunks - 1 else None)
+    torch.cuda.synchronize()
+    rows = boundary_rows(w.q_len, 16, extra=(1, 2))
+    idx = torch.from_numpy(rows).cuda()
+    ro, rl = oracle.chunk_partial(q, k, v, w.q_offset, 0, True, w.scale, rows=rows)
+    e_o, e_b, e_l = max_abs(o_acc[idx], ro), max_abs(ob[idx], ro), max_abs(l_acc[idx], rl)
+    print("fused ring: rows=%d max|do|=%.3g max|dbf16|=%.3g max|dlse|=%.3g" % (len(rows), e_o, e_b, e_l))
+    assert e_o <= TOL_BF16_OUT and e_b <= TOL_BF16_OUT and e_l <= TOL_BF16_LSE

@@ -25,6 +25,7 @@ SIGNATURES = {
     "hdp_attn_varlen_fwd": (I32, [P, P, P, P, I32, I32, I32, I32, F32, P, P, P]),
     "hdp_attn_varlen_fwd_f32": (I32, [P, P, P, P, I32, I32, I32, I32, F32, P, P, P]),
     "hdp_attn_chunk_partial": (I32, [P, I32, P, P, I32, I64, I64, I32, I32, I32, I32, F32, P, P, P]),
+    "hdp_attn_chunk_merge": (I32, [P, I32, P, P, I32, I64, I64, I32, I32, I32, I32, F32, P, P, P, P]),
     "hdp_lse_merge": (I32, [P, P, P, P, I32, I32, I32, P, P]),
     "hdp_attn_varlen_bwd": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, P]),
     "hdp_attn_varlen_bwd_noalloc": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, F32, P, P, P, P]),

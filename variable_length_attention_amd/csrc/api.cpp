@@ -299,17 +299,21 @@ int hdp_attn_varlen_fwd_f32(const float* q, const float* k, const float* v,
     return hdp::launch_fwd_f32(a, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 
-int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
-                           const void* v_chunk, int32_t Lk, int64_t q_offset, int64_t kv_offset,
-                           int32_t causal, int32_t H, int32_t Hkv, int32_t D, float scale,
-                           float* o_partial, float* lse, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The ring step's forward, either writing the partial (o, lse) or merging it into them.
+int chunk_forward(const void* q_slice, int32_t Lq, const void* k_chunk, const void* v_chunk, int32_t Lk,
+                  int64_t q_offset, int64_t kv_offset, int32_t causal, int32_t H, int32_t Hkv, int32_t D,
+                  float scale, float* o, float* lse, void* out_bf16, bool merge, hipStream_t stream) {
     if (Lq < 0 || Lk < 0 || q_offset < 0 || kv_offset < 0) return HDP_ERR_INVALID_ARG;
     if (int st = check_heads(H, Hkv, D)) return st;
     if (!std::isfinite(scale) || !(scale > 0.f)) return HDP_ERR_INVALID_ARG;
     if (q_offset > INT64_MAX / 4 || kv_offset > INT64_MAX / 4) return HDP_ERR_OVERFLOW;
     if (Lq > (1 << 30) || Lk > (1 << 30)) return HDP_ERR_OVERFLOW;
     if (Lq == 0) return HDP_OK;
-    if (!q_slice || !o_partial || !lse) return HDP_ERR_INVALID_ARG;
+    if (!q_slice || !o || !lse) return HDP_ERR_INVALID_ARG;
     if (Lk > 0 && (!k_chunk || !v_chunk)) return HDP_ERR_INVALID_ARG;
     int cus = 0;
     StreamState* st = nullptr;
@@ -321,8 +325,9 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
     a.H = H;
     a.Hkv = Hkv;
     a.scale_log2 = scale * kLog2e;
-    a.out = o_partial;
+    a.out = o;
     a.lse = lse;
+    a.out_bf16 = out_bf16;
     a.Lq = Lq;
     a.Lk = Lk;
     // Key j is visible to row r iff j <= (q_offset - kv_offset) + r; for 0 <= j < Lk and
@@ -332,7 +337,28 @@ int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
     a.causal = causal ? 1 : 0;
     int grid = 0;
     schedule(cus, st, H, Hkv, a, grid);
-    return hdp::launch_fwd_chunk(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+    const hipError_t e = merge ? hdp::launch_fwd_chunk_merge(a, D, grid, stream) : hdp::launch_fwd_chunk(a, D, grid, stream);
+    return e == hipSuccess ? HDP_OK : HDP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hdp_attn_chunk_partial(const void* q_slice, int32_t Lq, const void* k_chunk,
+                           const void* v_chunk, int32_t Lk, int64_t q_offset, int64_t kv_offset,
+                           int32_t causal, int32_t H, int32_t Hkv, int32_t D, float scale,
+                           float* o_partial, float* lse, hipStream_t stream) {
+    return chunk_forward(q_slice, Lq, k_chunk, v_chunk, Lk, q_offset, kv_offset, causal, H, Hkv, D, scale,
+                         o_partial, lse, nullptr, false, stream);
+}
+
+int hdp_attn_chunk_merge(const void* q_slice, int32_t Lq, const void* k_chunk, const void* v_chunk,
+                         int32_t Lk, int64_t q_offset, int64_t kv_offset, int32_t causal, int32_t H,
+                         int32_t Hkv, int32_t D, float scale, float* o_acc, float* lse_acc,
+                         void* out_bf16, hipStream_t stream) {
+    return chunk_forward(q_slice, Lq, k_chunk, v_chunk, Lk, q_offset, kv_offset, causal, H, Hkv, D, scale,
+                         o_acc, lse_acc, out_bf16, true, stream);
 }
 
 int hdp_lse_merge(float* o_acc, float* lse_acc, const float* o_part, const float* lse_part,

@@ -122,6 +122,13 @@ __device__ inline void buf_store_b128(void* base, uint32_t bytes, uint32_t off, 
 __device__ inline void buf_store_b32(void* base, uint32_t bytes, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), uniform_rsrc(base, bytes), off, 0, 0);
 }
+__device__ inline void buf_store_b64(void* base, uint32_t bytes, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, uniform_rsrc(base, bytes), off, 0, 0);
+}
+// Loads through the same kind of resource: a lane whose offset lies outside reads zeros.
+__device__ inline u32x4 buf_load_b128(const void* base, uint32_t bytes, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(uniform_rsrc(base, bytes), off, 0, 0);
+}
 // Beyond every resource the kernels build: the largest covers 32 rows of H <= 65535 heads of
 // 512-byte rows, under 2^30 bytes.
 constexpr uint32_t kDropOffset = 0x80000000u;

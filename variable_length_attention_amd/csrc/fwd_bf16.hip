@@ -5,7 +5,9 @@
 //   * varlen: many short sequences packed back to back, each attending only to itself under a
 //     causal mask (digest §3.1-§3.2, §4);
 //   * chunk: one slice of a long sequence against one key/value chunk of a ring step, with
-//     global positions (digest §3.2); the output is the normalised fp32 partial plus its lse.
+//     global positions (digest §3.2); the output is the normalised fp32 partial plus its lse;
+//   * chunk-merge: the same ring step, its partial merged by log-sum-exp into the running
+//     result in the epilogue instead of being written out for a separate merge pass.
 //
 // Layout of the work.  A workgroup of 4 waves takes one item = (sequence, head block, query
 // tile group).  With 4 or more query heads per key/value head, the 4 waves are 4 query heads
@@ -77,6 +79,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     static_assert(kRowsPerWave * C::kRowBytes <= C::kTileBytes && kRowsPerWave * C::kRowBytes <= 2 * 32 * kStageRowBytes,
                   "Q staging");
     __shared__ int s_item[8];
+    // merge mode: each output row's weight on the running accumulator, per wave
+    __shared__ float s_a1[MODE == 2 ? kWaves : 1][32];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
@@ -438,8 +442,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 const int row0 = r_lo + nt * 32;                   // first row of this tile
                 // rows row0 .. row0 + nrows - 1 of this tile exist (none past the sequence's end)
                 const int nrows = max(0, min(32, s_rows - row0));
+                float fs = inv;                                    // factor on the accumulator
+                float lout = lse;
+                if constexpr (MODE == 2) {
+                    // Merge into the running result by log-sum-exp: with w = exp(lse - m) over
+                    // m = max(lse_acc, lse), o = (w_acc o_acc + w o) / (w_acc + w) and
+                    // lse = m + ln(w_acc + w).  A row whose lse_acc is -inf has seen no key yet:
+                    // its o_acc is ignored; a partial with lse = -inf leaves the row as it was.
+                    const int r = row0 + l32;
+                    const float la = r < s_rows ? args.lse[(qbase + r) * (int64_t)H + head] : -INFINITY;
+                    float a1 = 0.f, a2 = 0.f;
+                    if (lse == -INFINITY) {
+                        a1 = la == -INFINITY ? 0.f : 1.f;
+                        lout = la;
+                    } else if (la == -INFINITY) {
+                        a2 = 1.f;
+                    } else {
+                        const float m = fmaxf(la, lse);
+                        const float w1 = __builtin_amdgcn_exp2f((la - m) * kLog2e);
+                        const float w2 = __builtin_amdgcn_exp2f((lse - m) * kLog2e);
+                        const float iw = 1.f / (w1 + w2);
+                        a1 = w1 * iw;
+                        a2 = w2 * iw;
+                        lout = m + __builtin_amdgcn_logf(w1 + w2) * kLn2;
+                    }
+                    fs = inv * a2;
+                    if (half == 0) s_a1[wave][l32] = a1;           // read back by the tile lanes
+                }
                 buf_store_b32(args.lse + (qbase + row0) * (int64_t)H + head, nrows > 0 ? (uint32_t)((nrows - 1) * H * 4 + 4) : 0u,
-                              half == 0 ? (uint32_t)(l32 * H * 4) : kDropOffset, lse);
+                              half == 0 ? (uint32_t)(l32 * H * 4) : kDropOffset, lout);
 #pragma unroll
                 for (int b = 0; b < kNB; ++b) {
                     // fragment -> tile: lane (row l32, half) holds d = mt*32 + 8*a4 + 4*half + 0..3
@@ -450,8 +481,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                         for (int a4 = 0; a4 < 4; ++a4) {
                             const int byte = (mt * 32 + 8 * a4 + 4 * half) * kE - b * kWb;
                             unsigned char* dst = tile + l32 * kWb + (((byte >> 4) ^ (l32 % kSlots)) << 4) + (byte & 15);
-                            const float x0 = oo[mt][nt][4 * a4 + 0] * inv, x1 = oo[mt][nt][4 * a4 + 1] * inv;
-                            const float x2 = oo[mt][nt][4 * a4 + 2] * inv, x3 = oo[mt][nt][4 * a4 + 3] * inv;
+                            const float x0 = oo[mt][nt][4 * a4 + 0] * fs, x1 = oo[mt][nt][4 * a4 + 1] * fs;
+                            const float x2 = oo[mt][nt][4 * a4 + 2] * fs, x3 = oo[mt][nt][4 * a4 + 3] * fs;
                             if (MODE == 0) {
                                 u32x2 w;
                                 w[0] = pack_bf16x2(x0, x1);
@@ -473,10 +504,43 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     }
                     unsigned char* gb = (unsigned char*)args.out + ((qbase + row0) * (int64_t)H + head) * kOutRow + b * kWb;
                     const uint32_t bytes = nrows > 0 ? (uint32_t)((nrows - 1) * H * kOutRow + kWb) : 0u;
+                    if constexpr (MODE == 2) {
+                        // o = a1 o_acc + (the tile, already scaled by a2); o_acc read where it is
+                        // written (rows past the slice's end read 0 and are not stored)
+                        u32x4 acc[kReads];
+#pragma unroll
+                        for (int i = 0; i < kReads; ++i) {
+                            const int tr = i * kRowsPerRead + lane / kSlots, slot = lane % kSlots;
+                            acc[i] = buf_load_b128(gb, bytes, (uint32_t)(tr * H * kOutRow + slot * 16));
+                        }
+#pragma unroll
+                        for (int i = 0; i < kReads; ++i) {
+                            const int tr = i * kRowsPerRead + lane / kSlots;
+                            const float a1 = s_a1[wave][tr];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float t = __uint_as_float(vals[i][e]);
+                                vals[i][e] = __float_as_uint(a1 != 0.f ? __builtin_fmaf(a1, __uint_as_float(acc[i][e]), t) : t);
+                            }
+                        }
+                    }
 #pragma unroll
                     for (int i = 0; i < kReads; ++i) {
                         const int tr = i * kRowsPerRead + lane / kSlots, slot = lane % kSlots;
                         buf_store_b128(gb, bytes, (uint32_t)(tr * H * kOutRow + slot * 16), vals[i]);
+                    }
+                    if (MODE == 2 && args.out_bf16 != nullptr) {
+                        // the merged result also as bf16 (half the byte offsets)
+                        unsigned char* gh = (unsigned char*)args.out_bf16 + ((qbase + row0) * (int64_t)H + head) * (kOutRow / 2) + b * (kWb / 2);
+                        const uint32_t hbytes = bytes / 2;
+#pragma unroll
+                        for (int i = 0; i < kReads; ++i) {
+                            const int tr = i * kRowsPerRead + lane / kSlots, slot = lane % kSlots;
+                            u32x2 w;
+                            w[0] = pack_bf16x2(__uint_as_float(vals[i][0]), __uint_as_float(vals[i][1]));
+                            w[1] = pack_bf16x2(__uint_as_float(vals[i][2]), __uint_as_float(vals[i][3]));
+                            buf_store_b64(gh, hbytes, (uint32_t)(tr * H * (kOutRow / 2) + slot * 8), w);
+                        }
                     }
                 }
             }
@@ -665,6 +729,12 @@ hipError_t launch_fwd_varlen(const FwdArgs& a, int D, int grid, hipStream_t s) {
 hipError_t launch_fwd_chunk(const FwdArgs& a, int D, int grid, hipStream_t s) {
     if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((fwd_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_chunk_merge(const FwdArgs& a, int D, int grid, hipStream_t s) {
+    if (D == 128) hipLaunchKernelGGL((fwd_kernel<128, 2>), dim3(grid), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<64, 2>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

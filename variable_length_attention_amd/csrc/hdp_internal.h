@@ -33,6 +33,9 @@ struct FwdArgs {
     int* counters;          // kCounterInts ints, zero on entry
     int32_t hpw;            // query heads per workgroup item (1, 2 or 4)
     int32_t nqueues;        // 8 (one per XCD) or 1
+    // chunk-merge mode: out / lse are the running o_acc / lse_acc (read and written); out_bf16
+    // is null or receives the merged result as bf16 [Lq][H][D]
+    void* out_bf16;
     // measurement: null, or kTraceWords words per workgroup (real-time counter at start and
     // end, items processed, unused)
     long long* trace;
@@ -97,6 +100,7 @@ struct BwdArgs {
 // Launchers (return hipSuccess or the launch error).  `grid` is the persistent grid size.
 hipError_t launch_fwd_varlen(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_chunk(const FwdArgs& a, int D, int grid, hipStream_t s);
+hipError_t launch_fwd_chunk_merge(const FwdArgs& a, int D, int grid, hipStream_t s);
 hipError_t launch_fwd_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 // Writes n zero ints at p with a kernel (not a memset node, so the call may be recorded into a

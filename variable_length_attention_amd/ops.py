@@ -128,6 +128,28 @@ def hdp_attn_chunk_partial(q_slice, k_chunk, v_chunk, q_offset: int, kv_offset: 
     return o_partial, lse
 
 
+def hdp_attn_chunk_merge(q_slice, k_chunk, v_chunk, q_offset: int, kv_offset: int, o_acc, lse_acc,
+                         causal: bool = True, scale=None, out_bf16=None) -> None:
+    """One ring step merged into the running (o_acc [Lq,H,D], lse_acc [Lq,H]) fp32, in place."""
+    for n, t in (("q_slice", q_slice), ("k_chunk", k_chunk), ("v_chunk", v_chunk)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("o_acc", o_acc, torch.float32, 3)
+    _dev_tensor("lse_acc", lse_acc, torch.float32, 2)
+    Lq, H, D = q_slice.shape
+    Lk, Hkv = k_chunk.shape[0], k_chunk.shape[1]
+    _shapes("hdp_attn_chunk_merge", k_chunk=(k_chunk, (Lk, Hkv, D)), v_chunk=(v_chunk, (Lk, Hkv, D)),
+            o_acc=(o_acc, (Lq, H, D)), lse_acc=(lse_acc, (Lq, H)))
+    if out_bf16 is not None:
+        _dev_tensor("out_bf16", out_bf16, torch.bfloat16, 3)
+        _shapes("hdp_attn_chunk_merge", out_bf16=(out_bf16, (Lq, H, D)))
+    _same_device("hdp_attn_chunk_merge", q_slice, k_chunk, v_chunk, o_acc, lse_acc, out_bf16)
+    st = _lib.lib().hdp_attn_chunk_merge(_ptr(q_slice), Lq, _ptr(k_chunk), _ptr(v_chunk), Lk,
+                                         int(q_offset), int(kv_offset), int(bool(causal)), H, Hkv, D,
+                                         _scale(D, scale), _ptr(o_acc), _ptr(lse_acc), _ptr(out_bf16),
+                                         _stream())
+    _lib.check("hdp_attn_chunk_merge", st)
+
+
 def hdp_lse_merge(o_acc, lse_acc, o_part, lse_part, out_bf16=None) -> None:
     """In place: (o_acc, lse_acc) <- merge((o_acc, lse_acc), (o_part, lse_part))."""
     _dev_tensor("o_acc", o_acc, torch.float32, 3)
