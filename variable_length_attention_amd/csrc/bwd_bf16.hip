@@ -567,8 +567,19 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
 
         // stage st -> ring buffer st % 4: Q and dO rows (clamped into the sequence) and the
         // rows' lse2 / delta (one 4-byte lane load each; lanes 0-31 lse2, 32-63 delta)
-        auto load_stage = [&](int st) {
-            const int ru = n_ru - 1 - st / G, hh = st % G;
+        // (row unit, head of the group) of a stage: row units from the last one down, the group's
+        // heads innermost.  Steps advance these by one stage at a time (no division per step).
+        struct StageAt { int st, ru, hh; };
+        auto stage_at = [&](int st) { return StageAt{st, n_ru - 1 - st / G, st % G}; };
+        auto advance = [&](StageAt& x) {
+            ++x.st;
+            if (++x.hh == G) {
+                x.hh = 0;
+                --x.ru;
+            }
+        };
+        auto load_stage = [&](const StageAt& x) {
+            const int st = x.st, ru = x.ru, hh = x.hh;
             const int head = g * G + hh;
             const int r0 = ru * kUnit;
             Stage& S = ring[st % kRing];
@@ -631,14 +642,14 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                 dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[ks]), __builtin_bit_cast(bf16x8, vf[ks]), dP, 0, 0, 0);
             }
         };
-        // invisible (key, row) pairs of stage st get S = -inf, so P = 0 and dS = 0
-        auto stage_full = [&](int st) {
-            const int r0 = (n_ru - 1 - st / G) * kUnit;
+        // invisible (key, row) pairs of a stage get S = -inf, so P = 0 and dS = 0
+        auto stage_full = [&](const StageAt& x) {
+            const int r0 = x.ru * kUnit;
             return (!causal || kt * kKeyTile + kKeyTile - 1 <= r0 + dpos) && r0 + kUnit <= s &&
                    kt * kKeyTile + kKeyTile <= sk;
         };
-        auto apply_mask = [&](int st, f32x16& S) {
-            const int r0 = (n_ru - 1 - st / G) * kUnit;
+        auto apply_mask = [&](const StageAt& x, f32x16& S) {
+            const int r0 = x.ru * kUnit;
             const int lim = min(s - 1 - r0, kUnit);     // rows r0 + jr with jr <= lim exist
             // visible iff jr >= kr: the key exists and (causal) key <= row + dpos
             const int kr = key >= sk ? kUnit : (causal ? max(key - dpos - r0, -1) : -1);
@@ -657,7 +668,9 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
             // prologue: stages 0 .. kAhead-1 loaded, stage 0 scored
 #pragma unroll
             for (int p = 0; p < kAhead; ++p)
-                if (p < n_st) load_stage(p);
+                if (p < n_st) load_stage(stage_at(p));
+            StageAt ld = stage_at(kAhead);             // the next stage to load
+            StageAt nx = stage_at(1);                  // the stage after the current one
             __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
             f32x16 SA, DA, SB, DB;
@@ -669,7 +682,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                 read_rows(0, 1, dr, 0, C::kKS);
                 sdp_full(qr, dr, SA, DA);
             }
-            if (!stage_full(0)) apply_mask(0, SA);
+            if (!stage_full(stage_at(0))) apply_mask(stage_at(0), SA);
 #pragma unroll
             for (int j = 0; j < 2; ++j) { PA[j] = bf16x8{}; TA[j] = bf16x8{}; }
 #pragma unroll
@@ -687,7 +700,8 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                     else __builtin_amdgcn_s_waitcnt(0x0F70);
                     __syncthreads();
                 }
-                if (st + kAhead < n_st) load_stage(st + kAhead);
+                if (st + kAhead < n_st) load_stage(ld);
+                advance(ld);
                 u32x4 qr[C::kKS], dr[C::kKS];
                 const int sn = min(st + 1, n_st - 1);     // past the end: harmless re-read
                 constexpr int kH = C::kKS / 2;             // second half read mid-way
@@ -745,7 +759,8 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                     Pc[h] = __builtin_bit_cast(bf16x8, u32x4{pw[4 * h], pw[4 * h + 1], pw[4 * h + 2], pw[4 * h + 3]});
                     Tc[h] = __builtin_bit_cast(bf16x8, u32x4{tw[4 * h], tw[4 * h + 1], tw[4 * h + 2], tw[4 * h + 3]});
                 }
-                if (st + 1 < n_st && !stage_full(st + 1)) apply_mask(st + 1, Sn);
+                if (st + 1 < n_st && !stage_full(nx)) apply_mask(nx, Sn);
+                advance(nx);
             };
             int st = 0;
             for (; st + 1 < n_st; st += 2) {
