@@ -63,6 +63,109 @@ __device__ inline void lds_dma4(const void* g, uint32_t lds) {
         : "=&s"(m0_saved) : "v"(g), "s"(lds) : "memory");
 }
 
+// Groups of direct global->LDS loads of 16 bytes per lane in the scalar-base form: lane l reads
+// at sbase + voff[i] (a uniform 64-bit base in SGPRs plus a 32-bit per-lane byte offset, so no
+// 64-bit vector address arithmetic per load) and the wave writes LDS at lds[i] + 16 * l.  Two
+// streams (two bases, e.g. K and V, or Q and dO) share the per-lane offsets: load i of stream s
+// goes to lds_s + 1024 * i.  M0 is saved once, set before each load with one wait state on
+// either side of the load, and restored once.  Ordering against LDS reads is the caller's, as
+// for lds_dma16.
+template <int N>
+__device__ inline void lds_dma16_pairs(const void* sbase0, const void* sbase1, const uint32_t (&voff)[N],
+                                       uint32_t lds0, uint32_t lds1) {
+    static_assert(N == 1 || N == 2 || N == 4, "groups of 1, 2 or 4 loads per stream");
+    uint32_t m0_saved;
+    if constexpr (N == 1) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %4\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %2\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %5\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %3\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "v"(voff[0]), "s"(sbase0), "s"(sbase1), "s"(lds0 + 0u), "s"(lds1 + 0u)
+            : "memory");
+    } else if constexpr (N == 2) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %5\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %3\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %6\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %3\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %7\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %4\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %8\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %4\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "v"(voff[0]), "v"(voff[1]), "s"(sbase0), "s"(sbase1), "s"(lds0 + 0u), "s"(lds0 + 1024u), "s"(lds1 + 0u), "s"(lds1 + 1024u)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %7\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %5\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %8\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %5\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %9\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %3, %5\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %10\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %4, %5\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %11\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %6\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %12\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %2, %6\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %13\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %3, %6\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %14\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %4, %6\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase0), "s"(sbase1), "s"(lds0 + 0u), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u), "s"(lds1 + 0u), "s"(lds1 + 1024u), "s"(lds1 + 2048u), "s"(lds1 + 3072u)
+            : "memory");
+    }
+}
+// One direct load of 4 bytes per lane in the scalar-base form (sbase + voff -> lds + 4 * lane).
+__device__ inline void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved) : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.693147180559945309f;
 

@@ -123,15 +123,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) kofs[j] = l32 * C::kRowBytes + 16 * ((2 * j) ^ t);
     }
-    // Stage loads: element offset of this lane's 16-byte chunk in each of its 1 KB blocks,
-    // relative to the stage's first key row of the head (the LDS slot of a chunk is fixed by
-    // the lane).
-    int gofs[C::kBlocksPerWave];
+    // Stage loads: byte offset of this lane's 16-byte chunk in each of its 1 KB blocks, relative
+    // to the stage's first key row of the head (the LDS slot of a chunk is fixed by the lane).
+    uint32_t gofs[C::kBlocksPerWave];
 #pragma unroll
     for (int i = 0; i < C::kBlocksPerWave; ++i) {
         const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
         const int chunk = (lane % C::kChunks) ^ swz(row);
-        gofs[i] = (int)(row * kv_stride + chunk * 8);
+        gofs[i] = (uint32_t)((row * kv_stride + chunk * 8) * 2);
     }
     // V^T: slot of D tile mt = (4 mt + c) ^ swz(tr_row), c = column / 8 within the tile
     int vofs[2];
@@ -280,29 +279,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // A whole stage inside the sequence takes a scalar base plus the per-lane offsets; the
         // last stage clamps its rows to the sequence's last key.
         auto load_stage = [&](int st, int B) {
-            unsigned char* kb = smem[B][0];
-            unsigned char* vb = smem[B][1];
             const int j0 = st * kStage;
+            // uniform base of the stage's first key row (scalar registers) + per-lane offsets
+            const int64_t sofs = (kbase + j0) * kv_stride + (int64_t)g * D;
+            uint32_t voff[C::kBlocksPerWave];
             if (j0 + kStage <= sk) {
 #pragma unroll
-                for (int i = 0; i < C::kBlocksPerWave; ++i) {
-                    const int blk = wave * C::kBlocksPerWave + i;
-                    const int64_t off = (kbase + j0) * kv_stride + (int64_t)g * D + gofs[i];
-                    lds_dma16(args.k + off, lds_addr(kb + blk * 1024));
-                    lds_dma16(args.v + off, lds_addr(vb + blk * 1024));
-                }
+                for (int i = 0; i < C::kBlocksPerWave; ++i) voff[i] = gofs[i];
             } else {
 #pragma unroll
                 for (int i = 0; i < C::kBlocksPerWave; ++i) {
-                    const int blk = wave * C::kBlocksPerWave + i;
-                    const int row = blk * C::kRowsPerBlock + lane / C::kChunks;
+                    const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
                     const int chunk = (lane % C::kChunks) ^ swz(row);
-                    const int j = min(j0 + row, sk - 1);
-                    const int64_t off = (kbase + j) * kv_stride + (int64_t)g * D + chunk * 8;
-                    lds_dma16(args.k + off, lds_addr(kb + blk * 1024));
-                    lds_dma16(args.v + off, lds_addr(vb + blk * 1024));
+                    const int j = min(j0 + row, sk - 1) - j0;
+                    voff[i] = (uint32_t)((j * kv_stride + chunk * 8) * 2);
                 }
             }
+            lds_dma16_pairs<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, voff,
+                                               lds_addr(smem[B][0] + wave * C::kBlocksPerWave * 1024),
+                                               lds_addr(smem[B][1] + wave * C::kBlocksPerWave * 1024));
         };
 
         // LDS base of unit u's rows in the K (kv = 0) or V (kv = 1) ring buffer: uniform
@@ -388,11 +383,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 tmax[nt] = xhalf_max(mx) * c2;
             }
         };
-        // P^T = exp2(S c2 - m) as bf16 B operands, row sums (fp32, before rounding) into ll
-        auto exponentials = [&](const f32x16 (&S)[kNT], const float (&mm)[kNT], float (&ll)[kNT], bf16x8 (&P)[kNT][2]) {
+        // P^T = exp2(S c2 - mr) as bf16 B operands, row sums (fp32, before rounding) into ll
+        auto exponentials = [&](const f32x16 (&S)[kNT], const float (&mr)[kNT], float (&ll)[kNT], bf16x8 (&P)[kNT][2]) {
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                const float mb = (mm[nt] == -INFINITY) ? 0.f : mm[nt];
+                const float mb = mr[nt];
                 float ls = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -559,9 +554,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         for (int mt = 0; mt < C::kMT; ++mt)
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) o[mt][nt] = f32x16{};
-        float m[kNT], l[kNT], thr[kNT];
+        // m: the reference (-inf before a row's first visible key); mref: the value subtracted
+        // in the exponentials (0 while m is -inf), kept beside m so the steps need not derive it
+        float m[kNT], mref[kNT], l[kNT], thr[kNT];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; l[nt] = 0.f; thr[nt] = -1.f; }
+        for (int nt = 0; nt < kNT; ++nt) { m[nt] = -INFINITY; mref[nt] = 0.f; l[nt] = 0.f; thr[nt] = -1.f; }
 
         // Runs when some lane's unit sum ls passed its threshold: raises the reference to the
         // row max (in log2 units), rescales what was accumulated before this unit (its sum lb)
@@ -579,12 +576,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     const float mn = fmaxf(m[nt], tmax[nt]);
                     const float alpha = (m[nt] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[nt] - mn);
                     m[nt] = mn;
+                    mref[nt] = (mn == -INFINITY) ? 0.f : mn;
                     l[nt] = lb[nt] * alpha;
                     thr[nt] = (mn == -INFINITY) ? -1.f : kLazySum;
 #pragma unroll
                     for (int mt = 0; mt < C::kMT; ++mt) o[mt][nt] *= alpha;
                 }
-                exponentials(S, m, l, P);
+                exponentials(S, mref, l, P);
             }
         };
 
@@ -612,11 +610,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             constexpr int kQK = C::kKS * kNT;
             constexpr int kElems = 16 * kNT;                       // score elements per lane
             constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
-            float mb[kNT], ls[kNT], lb[kNT], pe = 0.f;
+            float ls[kNT], lb[kNT], pe = 0.f;
+            const float (&mb)[kNT] = mref;
             uint32_t pw[kNT][8];                                   // P as bf16 pairs
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-                mb[nt] = (m[nt] == -INFINITY) ? 0.f : m[nt];
                 ls[nt] = 0.f;
                 lb[nt] = l[nt];
                 Sn[nt] = f32x16{};
