@@ -14,6 +14,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -151,6 +152,57 @@ __device__ inline void lds_dma16_pairs(const void* sbase0, const void* sbase1, c
             "s_mov_b32 m0, %0"
             : "=&s"(m0_saved)
             : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase0), "s"(sbase1), "s"(lds0 + 0u), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u), "s"(lds1 + 0u), "s"(lds1 + 1024u), "s"(lds1 + 2048u), "s"(lds1 + 3072u)
+            : "memory");
+    }
+}
+// Two tiles of N direct global->LDS loads of 16 bytes per lane in the scalar-base form, with
+// one M0 write per tile: the instruction's immediate offset moves the global and the LDS address
+// alike, so load i of stream s reads sbase_s + voffb[i] + 1024 i and writes lds_s + 1024 i +
+// 16 * lane.  voffb[i] is therefore the lane's byte offset of block i minus 1024 i (it must not
+// be negative: the per-lane offset is unsigned).  One wait state separates each M0 write from
+// the loads that read it.  Ordering against LDS reads is the caller's, as for lds_dma16.
+template <int N>
+__device__ inline void lds_dma16_tiles(const void* sbase0, const void* sbase1, const uint32_t (&voffb)[N],
+                                       uint32_t lds0, uint32_t lds1) {
+    static_assert(N == 2 || N == 4, "tiles of 2 or 4 loads");
+    uint32_t m0_saved;
+    if constexpr (N == 2) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %5\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %3\n\t"
+            "global_load_lds_dwordx4 %2, %3 offset:1024\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %6\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %4\n\t"
+            "global_load_lds_dwordx4 %2, %4 offset:1024\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "v"(voffb[0]), "v"(voffb[1]), "s"(sbase0), "s"(sbase1), "s"(lds0), "s"(lds1)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %7\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %5\n\t"
+            "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+            "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+            "global_load_lds_dwordx4 %4, %5 offset:3072\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %8\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %6\n\t"
+            "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
+            "global_load_lds_dwordx4 %3, %6 offset:2048\n\t"
+            "global_load_lds_dwordx4 %4, %6 offset:3072\n\t"
+            "s_nop 0\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "v"(voffb[0]), "v"(voffb[1]), "v"(voffb[2]), "v"(voffb[3]), "s"(sbase0), "s"(sbase1), "s"(lds0), "s"(lds1)
             : "memory");
     }
 }

@@ -130,7 +130,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     for (int i = 0; i < C::kBlocksPerWave; ++i) {
         const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
         const int chunk = (lane % C::kChunks) ^ swz(row);
-        gofs[i] = (uint32_t)((row * kv_stride + chunk * 8) * 2);
+        // minus the block's LDS offset, which the load instruction's immediate adds back to
+        // both addresses (row >= 4 i for D = 128, >= 8 i for D = 64, so this stays >= 0)
+        gofs[i] = (uint32_t)((row * kv_stride + chunk * 8) * 2) - 1024u * i;
     }
     // V^T: slot of D tile mt = (4 mt + c) ^ swz(tr_row), c = column / 8 within the tile
     int vofs[2];
@@ -282,11 +284,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             const int j0 = st * kStage;
             // uniform base of the stage's first key row (scalar registers) + per-lane offsets
             const int64_t sofs = (kbase + j0) * kv_stride + (int64_t)g * D;
-            uint32_t voff[C::kBlocksPerWave];
+            const uint32_t lk = lds_addr(smem[B][0] + wave * C::kBlocksPerWave * 1024);
+            const uint32_t lv = lds_addr(smem[B][1] + wave * C::kBlocksPerWave * 1024);
             if (j0 + kStage <= sk) {
-#pragma unroll
-                for (int i = 0; i < C::kBlocksPerWave; ++i) voff[i] = gofs[i];
+                lds_dma16_tiles<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, gofs, lk, lv);
             } else {
+                uint32_t voff[C::kBlocksPerWave];
 #pragma unroll
                 for (int i = 0; i < C::kBlocksPerWave; ++i) {
                     const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
@@ -294,10 +297,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     const int j = min(j0 + row, sk - 1) - j0;
                     voff[i] = (uint32_t)((j * kv_stride + chunk * 8) * 2);
                 }
+                lds_dma16_pairs<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, voff, lk, lv);
             }
-            lds_dma16_pairs<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, voff,
-                                               lds_addr(smem[B][0] + wave * C::kBlocksPerWave * 1024),
-                                               lds_addr(smem[B][1] + wave * C::kBlocksPerWave * 1024));
         };
 
         // LDS base of unit u's rows in the K (kv = 0) or V (kv = 1) ring buffer: uniform
@@ -596,6 +597,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // diagonal or the last key, i.e. at the end of an item).  Steps go in pairs that swap
         // the roles of two score and two probability buffers, so no registers are copied
         // between steps.
+        // row sum and bf16 packing of score element e (P value pe, the previous element's pp)
+        auto sum_pack = [&](int e, float pp, float pe, float (&ls)[kNT], uint32_t (&pw)[kNT][8]) {
+            const int nt = e / 16, i = e % 16;
+            ls[nt] = i == 0 ? pe : ls[nt] + pe;
+            if (i & 1) {
+                // the empty asm anchors the conversion in this slot (otherwise it drifts to the
+                // end of the step, or into the rare branch)
+                pw[nt][i >> 1] = pack_bf16x2(pp, pe);
+                asm volatile("" : "+v"(pw[nt][i >> 1]));
+            }
+        };
         bf16x8 vf[2][C::kMT];
         auto step = [&](int u, bool odd, f32x16 (&Sc)[kNT], f32x16 (&Sn)[kNT], const bf16x8 (&Pp)[kNT][2],
                         bf16x8 (&Pc)[kNT][2]) {
@@ -610,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             constexpr int kQK = C::kKS * kNT;
             constexpr int kElems = 16 * kNT;                       // score elements per lane
             constexpr int kSlots = (kPV + kQK) > kElems ? (kPV + kQK) : kElems;
-            float ls[kNT], lb[kNT], pe = 0.f;
+            float ls[kNT], lb[kNT], p1 = 0.f, p2 = 0.f;       // P of the two previous elements
             const float (&mb)[kNT] = mref;
             uint32_t pw[kNT][8];                                   // P as bf16 pairs
 #pragma unroll
@@ -635,22 +647,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     Sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, qf[nt][ks]), Sn[nt], 0, 0, 0);
                 }
-                // score element e = k of this unit
+                // score element e = k of this unit: its exponential here, its sum and bf16
+                // packing one slot later, so that no instruction right after v_exp reads its
+                // result (a transcendental result needs a wait state before a VALU reads it)
                 if (k < kElems) {
                     const int nt = k / 16, i = k % 16;
                     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[nt][i], c2, -mb[nt]));
-                    ls[nt] = i == 0 ? pv : ls[nt] + pv;
-                    if (i & 1) {
-                        // pack the pair in this slot; the empty asm anchors the conversion here
-                        // (otherwise it drifts to the end of the step, or into the rare branch)
-                        pw[nt][i >> 1] = pack_bf16x2(pe, pv);
-                        asm volatile("" : "+v"(pw[nt][i >> 1]));
-                    } else {
-                        pe = pv;
-                    }
+                    if (k > 0) sum_pack(k - 1, p2, p1, ls, pw);
+                    p2 = p1;
+                    p1 = pv;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            sum_pack(kElems - 1, p2, p1, ls, pw);
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 l[nt] += ls[nt];
