@@ -10,7 +10,7 @@
 // A row-values pass and one persistent kernel with two bodies, no atomics on gradients, so
 // every gradient is deterministic:
 //   * row values: lse in log2 units and delta = rowsum(dO * O) of every (row, head), written
-//     head-major ([2][H][T]: rows of one head contiguous) for the dK/dV body;
+//     head-major as pairs ([H][T][2]: the rows of one head contiguous) for the dK/dV body;
 //   * dK/dV body, key-major (one item = 128 keys of one key/value head, 32 keys per wave):
 //         S = Q K^T,  dP = dO V^T,  dS = P * (dP - delta),  dV += P^T dO,  dK += dS^T Q,
 //     for every 32-row unit of the sequence at or after the keys and every query head of the
@@ -120,7 +120,7 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
     using C = Cfg<D>;
     constexpr int kTile = kStage * C::kRowBytes;
     constexpr int kBPW = kStage / C::kRowsPerBlock / kWaves;   // 1 KB stage loads per wave and tile
-    auto smem = (unsigned char (*)[2][kTile])lds;              // [kStages][K, V][tile]
+    // LDS: kStages ring buffers of [K tile][V tile], then the two item slots
     int* s_item = (int*)(lds + kStages * 2 * kTile);
 
     const int tid = threadIdx.x;
@@ -155,12 +155,17 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
 #pragma unroll
         for (int j = 0; j < 2; ++j) tofs[j] = tr_row * C::kRowBytes + 16 * ((4 * j) ^ t) + (lane & 1) * 8;
     }
-    int grow[kBPW], gchunk[kBPW];
+    // whole-stage loads: this lane's byte offset in each of its 1 KB blocks from the stage's
+    // first key row of the head, minus the block's LDS offset that the load instruction's
+    // immediate adds back to both addresses (row >= kRowsPerBlock i keeps it >= 0)
+    uint32_t voffk[kBPW];
 #pragma unroll
     for (int i = 0; i < kBPW; ++i) {
-        grow[i] = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
-        gchunk[i] = (lane % C::kChunks) ^ swz(grow[i]);
+        const int row = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
+        const int chunk = (lane % C::kChunks) ^ swz(row);
+        voffk[i] = (uint32_t)((row * kv_stride + chunk * 8) * 2) - 1024u * i;
     }
+    const uint32_t ring0 = lds_addr(lds);              // LDS byte address of stage buffer 0
 
     QueuePlan plan{0, 0, 0, 0, 0, 0, 0, 0};
     if (wave == 0) {
@@ -216,22 +221,31 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
         const int n_stages = (n_units + 1) / 2;
         const int64_t kbase = MODE == 0 ? base : 0;
 
-        // stage st (64 keys, clamped into the key range) into ring buffer st % 3
-        auto load_stage = [&](int st) {
-            unsigned char* kb = smem[st % kStages][0];
-            unsigned char* vb = smem[st % kStages][1];
+        // stage st (64 keys) into ring buffer buf (= st mod 3); the last stage clamps its rows
+        // into the key range
+        auto load_stage = [&](int st, int buf) {
+            const uint32_t lk = ring0 + (uint32_t)buf * (2 * kTile) + wave * kBPW * 1024;
+            const int j0 = st * kStage;
+            if (j0 + kStage <= sk) {
+                const int64_t sofs = (kbase + j0) * kv_stride + (int64_t)g * D;
+                lds_dma16_tiles<kBPW>(args.k + sofs, args.v + sofs, voffk, lk, lk + kTile);
+            } else {
 #pragma unroll
-            for (int i = 0; i < kBPW; ++i) {
-                const int blk = wave * kBPW + i;
-                const int64_t off = (kbase + min(st * kStage + grow[i], sk - 1)) * kv_stride + (int64_t)g * D + gchunk[i] * 8;
-                lds_dma16(args.k + off, lds_addr(kb + blk * 1024));
-                lds_dma16(args.v + off, lds_addr(vb + blk * 1024));
+                for (int i = 0; i < kBPW; ++i) {
+                    const int row = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
+                    const int chunk = (lane % C::kChunks) ^ swz(row);
+                    const int64_t off = (kbase + min(j0 + row, sk - 1)) * kv_stride + (int64_t)g * D + chunk * 8;
+                    lds_dma16(args.k + off, lk + 1024 * i);
+                    lds_dma16(args.v + off, lk + kTile + 1024 * i);
+                }
             }
         };
         if (n_units > 0) {
-            load_stage(0);
-            if (n_stages > 1) load_stage(1);
+            load_stage(0, 0);
+            if (n_stages > 1) load_stage(1, 1);
         }
+        int lbuf = 2;                                    // ring buffer of the next stage load
+        int cbuf = 0;                                    // ring buffer of the current unit's stage
 
         // Q^T and dO^T fragments; lse in log2 units and delta from the row-values pass
         u32x4 qf[C::kKS], df[C::kKS];
@@ -244,25 +258,23 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             }
         }
         const int Trv = MODE == 0 ? args.T : args.Lq;    // row stride of the lse2/delta planes
-        const float lse2 = row_ok ? args.rowvals[(int64_t)head * Trv + base + row] : 0.f;
-        const float delta = row_ok ? args.rowvals[((int64_t)H + head) * Trv + base + row] : 0.f;
+        const f32x2 rv = row_ok ? *(const f32x2*)(args.rowvals + 2 * ((int64_t)head * Trv + base + row)) : f32x2{0.f, 0.f};
+        const float lse2 = rv[0], delta = rv[1];
         wait_vm0();
         __syncthreads();
 
-        auto unit_base = [&](int u, int kv) {
-            return (uint32_t)__builtin_amdgcn_readfirstlane(
-                (int)(lds_addr(smem[(u >> 1) % kStages][kv]) + (u & 1) * 32 * C::kRowBytes));
-        };
-        auto read_rows = [&](int u, int kv, u32x4 (&f)[C::kKS]) {
-            const uint32_t b = unit_base(u, kv);
+        // LDS byte address of the 32 rows of a unit: ring buffer buf, half h of its stage
+        auto unit_base = [&](int buf, int h) { return ring0 + (uint32_t)buf * (2 * kTile) + (uint32_t)h * (32 * C::kRowBytes); };
+        auto read_rows = [&](uint32_t ub, int kv, u32x4 (&f)[C::kKS]) {
+            const uint32_t b = ub + kv * kTile;
             uint32_t a[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) a[j] = lds_add(b, rofs[j]);
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks) f[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
         };
-        auto read_cols = [&](int u, int kv, bf16x8 (&f)[2][C::kMT]) {
-            const uint32_t b = unit_base(u, kv);
+        auto read_cols = [&](uint32_t ub, int kv, bf16x8 (&f)[2][C::kMT]) {
+            const uint32_t b = ub + kv * kTile;
             const uint32_t a[2] = {lds_add(b, tofs[0]), lds_add(b, tofs[1])};
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
@@ -291,7 +303,8 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             wait_vm0();
             __syncthreads();
             const int st = (u + 3) >> 1;
-            if (st < n_stages) load_stage(st);
+            if (st < n_stages) load_stage(st, lbuf);
+            lbuf = lbuf == kStages - 1 ? 0 : lbuf + 1;
         };
 
         f32x16 acc[C::kMT];
@@ -305,9 +318,12 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
                         const bf16x8 (&Tp)[2], bf16x8 (&Tc)[2]) {
             if (odd) stage_turn(u);
             u32x4 kf[C::kKS], vf[C::kKS];
-            const int un = min(u + 1, n_units - 1);      // past the end: harmless re-read
-            read_rows(un, 0, kf);
-            read_rows(un, 1, vf);
+            // rows of unit u + 1: the second half of this stage (u even) or the first half of
+            // the next (u odd); past the end, unit u again (a harmless re-read)
+            const int nbuf = cbuf == kStages - 1 ? 0 : cbuf + 1;
+            const uint32_t un_base = u + 1 >= n_units ? unit_base(cbuf, odd) : odd ? unit_base(nbuf, 0) : unit_base(cbuf, 1);
+            read_rows(un_base, 0, kf);
+            read_rows(un_base, 1, vf);
             __builtin_amdgcn_sched_barrier(0);
             constexpr int kDQ = 2 * C::kMT;              // dQ MFMAs
             constexpr int kSD = 2 * C::kKS;              // S and dP MFMAs
@@ -317,7 +333,7 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
 #pragma unroll
             for (int k = 0; k < kSlots; ++k) {
                 if (k == kDQ) {
-                    read_cols(u, 0, kt);                 // K^T of unit u, for the next step
+                    read_cols(unit_base(cbuf, odd), 0, kt);   // K^T of unit u, for the next step
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (k < kDQ) {
@@ -347,6 +363,7 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             for (int h = 0; h < 2; ++h)
                 Tc[h] = __builtin_bit_cast(bf16x8, u32x4{tw[4 * h], tw[4 * h + 1], tw[4 * h + 2], tw[4 * h + 3]});
             if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
+            if (odd) cbuf = nbuf;
         };
 
         if (n_units > 0) {
@@ -360,8 +377,8 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             TA[1] = bf16x8{};
             {
                 u32x4 kf[C::kKS], vf[C::kKS];
-                read_rows(0, 0, kf);
-                read_rows(0, 1, vf);
+                read_rows(unit_base(0, 0), 0, kf);
+                read_rows(unit_base(0, 0), 1, vf);
                 SA = f32x16{};
                 DA = f32x16{};
 #pragma unroll
@@ -430,10 +447,10 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
 // rows, query head of the group) from the end of the sequence down to the diagonal.  Step st issues
 // the dV/dK products of stage st-1 (16 MFMAs) and the S/dP products of stage st+1 (16 MFMAs)
 // around the elementwise part of stage st (P = exp2(S c - lse2), dS = P (dP - delta)), one
-// element per slot.  Q and dO tiles (32 rows each) and the stage's 32 lse2 and delta values
-// arrive in LDS through direct global->LDS loads, in a ring of four stages two steps ahead.
-// eight stages of a Q tile, a dO tile (32 rows each) and the 32 rows' lse2 and delta, plus the
-// two item slots (the layout is checked against the body's own in a static_assert)
+// element per slot.  Q and dO tiles (32 rows each) and the stage's 32 (lse2, delta) pairs
+// arrive in LDS through direct global->LDS loads, in a ring of eight stages five steps ahead.
+// LDS: the eight stages plus the two item slots (the layout is checked against the body's own
+// in a static_assert)
 template <int D>
 constexpr int dkdv_lds_bytes() { return 8 * (2 * kUnit * Cfg<D>::kRowBytes + 2 * kUnit * 4) + 8 * (int)sizeof(int); }
 
@@ -455,9 +472,11 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
     struct Stage {
         unsigned char q[kTile];
         unsigned char d[kTile];
-        float rv[2][kUnit];                                // lse2, delta of the 32 rows
+        float rv[kUnit][2];                                // (lse2, delta) of the 32 rows
     };
     static_assert(kRing * sizeof(Stage) + 8 * sizeof(int) == (size_t)dkdv_lds_bytes<D>(), "LDS layout");
+    constexpr uint32_t kStageBytes = sizeof(Stage);
+    constexpr uint32_t kRvOfs = 2 * kTile;                 // byte offset of rv in a stage
     Stage* ring = (Stage*)lds;
     int* s_item = (int*)(lds + kRing * sizeof(Stage));
 
@@ -492,12 +511,17 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
 #pragma unroll
         for (int j = 0; j < 2; ++j) tofs[j] = tr_row * C::kRowBytes + 16 * ((4 * j) ^ t) + (lane & 1) * 8;
     }
-    int grow[kBPW], gchunk[kBPW];
+    // whole-stage loads: this lane's byte offset in each of its 1 KB blocks from the stage's
+    // first row of the head, minus the block's LDS offset that the load instruction's immediate
+    // adds back to both addresses (row >= kRowsPerBlock i, so the difference stays >= 0)
+    uint32_t voffq[kBPW];
 #pragma unroll
     for (int i = 0; i < kBPW; ++i) {
-        grow[i] = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
-        gchunk[i] = (lane % C::kChunks) ^ swz(grow[i]);
+        const int row = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
+        const int chunk = (lane % C::kChunks) ^ swz(row);
+        voffq[i] = (uint32_t)((row * q_stride + chunk * 8) * 2) - 1024u * i;
     }
+    const uint32_t ring0 = lds_addr(lds);              // LDS byte address of stage buffer 0
 
     QueuePlan plan{0, 0, 0, 0, 0, 0, 0, 0};
     if (wave == 0) {
@@ -565,8 +589,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
             }
         }
 
-        // stage st -> ring buffer st % 4: Q and dO rows (clamped into the sequence) and the
-        // rows' lse2 / delta (one 4-byte lane load each; lanes 0-31 lse2, 32-63 delta)
+        // stage st -> ring buffer st mod 8: Q and dO rows and the rows' (lse2, delta) pairs.
         // (row unit, head of the group) of a stage: row units from the last one down, the group's
         // heads innermost.  Steps advance these by one stage at a time (no division per step).
         struct StageAt { int st, ru, hh; };
@@ -578,59 +601,74 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                 --x.ru;
             }
         };
+        // LDS byte address of stage st's buffer (uniform)
+        auto stage_lds = [&](int st) { return ring0 + (uint32_t)(st & (kRing - 1)) * kStageBytes; };
         auto load_stage = [&](const StageAt& x) {
-            const int st = x.st, ru = x.ru, hh = x.hh;
-            const int head = g * G + hh;
-            const int r0 = ru * kUnit;
-            Stage& S = ring[st % kRing];
+            const int head = g * G + x.hh;
+            const int r0 = x.ru * kUnit;
+            const uint32_t lq = stage_lds(x.st) + wave * kBPW * 1024;
+            const uint32_t lrv = stage_lds(x.st) + kRvOfs;
+            // every wave loads the same 256 bytes of row values (32 rows x (lse2, delta)), so
+            // all waves count the same memory ops.  The chunk form (fp32 read-modify-write
+            // epilogue) keeps the per-load path: with both paths it no longer fits its registers.
+            if (MODE == 0 && r0 + kUnit <= s) {
+                const int64_t sofs = (base + r0) * q_stride + (int64_t)head * D;
+                if constexpr (kBPW == 1) lds_dma16_pairs<1>(args.q + sofs, args.dout + sofs, voffq, lq, lq + kTile);
+                else lds_dma16_tiles<kBPW>(args.q + sofs, args.dout + sofs, voffq, lq, lq + kTile);
+                lds_dma4_s(args.rowvals + 2 * ((int64_t)head * Trv + base + r0), 4u * lane, lrv);
+            } else {
+                // the stage at the sequence's end: rows clamped to its last row
 #pragma unroll
-            for (int i = 0; i < kBPW; ++i) {
-                const int blk = wave * kBPW + i;
-                const int64_t off = (base + min(r0 + grow[i], s - 1)) * q_stride + (int64_t)head * D + gchunk[i] * 8;
-                lds_dma16(args.q + off, lds_addr(S.q + blk * 1024));
-                lds_dma16(args.dout + off, lds_addr(S.d + blk * 1024));
-            }
-            {   // every wave loads the same 256 bytes, so all count the same memory ops
-                const int64_t r = base + min(r0 + l32, s - 1);
-                const float* src = args.rowvals + ((int64_t)half * H + head) * Trv + r;
-                lds_dma4(src, lds_addr(&S.rv[0][0]));
+                for (int i = 0; i < kBPW; ++i) {
+                    const int row = (wave * kBPW + i) * C::kRowsPerBlock + lane / C::kChunks;
+                    const int chunk = (lane % C::kChunks) ^ swz(row);
+                    const int64_t off = (base + min(r0 + row, s - 1)) * q_stride + (int64_t)head * D + chunk * 8;
+                    lds_dma16(args.q + off, lq + 1024 * i);
+                    lds_dma16(args.dout + off, lq + kTile + 1024 * i);
+                }
+                const int64_t rr = (int64_t)head * Trv + base + min(r0 + (lane >> 1), s - 1);
+                lds_dma4(args.rowvals + 2 * rr + (lane & 1), lrv);
             }
         };
-        auto tile_base = [&](int st, int which) {   // uniform LDS address of a stage's tile
-            Stage& S = ring[st % kRing];
-            return (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(which == 0 ? S.q : S.d));
-        };
-        // A-operand row fragments of a tile (Q or dO rows), k-steps ks0 .. ks0 + n - 1 over D
-        auto read_rows = [&](int st, int which, u32x4 (&f)[C::kKS], int ks0, int n) {
-            const uint32_t b = tile_base(st, which);
-            uint32_t a[4];
+        // A-operand row fragments (Q rows: which = 0, dO rows: which = 1) of the stage whose
+        // per-lane row addresses are ra, k-steps ks0 .. ks0 + n - 1 over D
+        auto rows_addr = [&](int st, uint32_t (&ra)[4]) {
+            const uint32_t b = stage_lds(st);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a[j] = lds_add(b, rofs[j]);
+            for (int j = 0; j < 4; ++j) ra[j] = lds_add(b, rofs[j]);
+        };
+        auto read_rows = [&](const uint32_t (&ra)[4], int which, u32x4 (&f)[C::kKS], int ks0, int n) {
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks)
-                if (ks >= ks0 && ks < ks0 + n) f[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
+                if (ks >= ks0 && ks < ks0 + n)
+                    f[ks] = *(const lds_u32x4*)(uintptr_t)(ra[ks & 3] + which * kTile + 128 * (ks >> 2));
         };
         // B-operand transposed fragments: for k-step ks2 and D tile mt, lane l receives column
         // mt*32 + l%32 of rows 16 ks2 + 8 (i/4) + 4 (l/32) + i%4 (the accumulator row order)
-        auto read_cols = [&](int st, int which, bf16x8 (&f)[2][C::kMT]) {
-            const uint32_t b = tile_base(st, which);
+        auto read_cols = [&](int st, bf16x8 (&fd)[2][C::kMT], bf16x8 (&fq)[2][C::kMT]) {
+            const uint32_t b = stage_lds(st);
             const uint32_t a[2] = {lds_add(b, tofs[0]), lds_add(b, tofs[1])};
 #pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2)
+            for (int which = 1; which >= 0; --which)
 #pragma unroll
-                for (int mt = 0; mt < C::kMT; ++mt) {
-                    const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
-                    f[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
-                    f[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
-                }
+                for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+                    for (int mt = 0; mt < C::kMT; ++mt) {
+                        const uint32_t p0 = a[mt & 1] + which * kTile + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
+                        bf16x8& f = which ? fd[ks2][mt] : fq[ks2][mt];
+                        f.lo = __builtin_bit_cast(bf16x4, lo);
+                        f.hi = __builtin_bit_cast(bf16x4, hi);
+                    }
         };
-        // lse2 and delta of the lane's accumulator rows 8*j + 4*half + (0..3) (elements 4j..4j+3)
-        auto read_rowvals = [&](int st, int j, f32x4& l2, f32x4& dl) {
-            const Stage& S = ring[st % kRing];
-            l2 = *(const f32x4*)&S.rv[0][8 * j + 4 * half];
-            dl = *(const f32x4*)&S.rv[1][8 * j + 4 * half];
+        // lse2 and delta of the lane's accumulator rows 8*j + 4*half + (0..3) (elements 4j..4j+3):
+        // four (lse2, delta) pairs at rva + 64 j
+        auto read_rowvals = [&](uint32_t rva, int j, f32x4& l2, f32x4& dl) {
+            const f32x4 a = __builtin_bit_cast(f32x4, *(const lds_u32x4*)(uintptr_t)(rva + 64 * j));
+            const f32x4 b = __builtin_bit_cast(f32x4, *(const lds_u32x4*)(uintptr_t)(rva + 64 * j + 16));
+            l2 = f32x4{a[0], a[2], b[0], b[2]};
+            dl = f32x4{a[1], a[3], b[1], b[3]};
         };
         // S (rows x keys) = Q K^T and dP = dO V^T of one stage from its row fragments
         auto sdp_full = [&](const u32x4 (&qr)[C::kKS], const u32x4 (&dr)[C::kKS], f32x16& S, f32x16& dP) {
@@ -678,8 +716,10 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
             bf16x8 dt[2][C::kMT], qt[2][C::kMT];
             {
                 u32x4 qr[C::kKS], dr[C::kKS];
-                read_rows(0, 0, qr, 0, C::kKS);
-                read_rows(0, 1, dr, 0, C::kKS);
+                uint32_t ra[4];
+                rows_addr(0, ra);
+                read_rows(ra, 0, qr, 0, C::kKS);
+                read_rows(ra, 1, dr, 0, C::kKS);
                 sdp_full(qr, dr, SA, DA);
             }
             if (!stage_full(stage_at(0))) apply_mask(stage_at(0), SA);
@@ -691,40 +731,60 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                 for (int mt = 0; mt < C::kMT; ++mt) { dt[ks2][mt] = bf16x8{}; qt[ks2][mt] = bf16x8{}; }
 
             // step st: dV/dK of st-1 (operands Pp, Tp, dt, qt), S/dP of st+1 into Sn/Dn, the
-            // elementwise part of st from Sc/Dc into Pc/Tc
+            // elementwise part of st from Sc/Dc into Pc/Tc.  ph = st mod kSyncEvery.
+            int ph = 0;
             auto step = [&](int st, f32x16& Sc, f32x16& Dc, f32x16& Sn, f32x16& Dn,
                             const bf16x8 (&Pp)[2], const bf16x8 (&Tp)[2], bf16x8 (&Pc)[2], bf16x8 (&Tc)[2]) {
                 __builtin_amdgcn_sched_barrier(0);          // steps stay apart in the schedule
-                if (st > 0 && st % kSyncEvery == 0) {
+                if (st > 0 && ph == 0) {
                     if (st - 1 + kAhead < n_st) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerStage);
                     else __builtin_amdgcn_s_waitcnt(0x0F70);
                     __syncthreads();
                 }
+                ph = ph == kSyncEvery - 1 ? 0 : ph + 1;
                 if (st + kAhead < n_st) load_stage(ld);
                 advance(ld);
                 u32x4 qr[C::kKS], dr[C::kKS];
                 const int sn = min(st + 1, n_st - 1);     // past the end: harmless re-read
                 constexpr int kH = C::kKS / 2;             // second half read mid-way
-                read_rows(sn, 0, qr, 0, kH);
-                read_rows(sn, 1, dr, 0, kH);
+                {
+                    uint32_t ra[4];
+                    rows_addr(sn, ra);
+                    read_rows(ra, 0, qr, 0, kH);
+                    read_rows(ra, 1, dr, 0, kH);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 uint32_t pw[8], tw[8];
                 float pe = 0.f, te = 0.f;
                 f32x4 l2[2], dl[2];                        // rows of element groups j, j+1
-                read_rowvals(st, 0, l2[0], dl[0]);
+                const uint32_t rva = lds_add(stage_lds(st) + kRvOfs, 32u * half);
+                read_rowvals(rva, 0, l2[0], dl[0]);
+                // t = P (dP - delta) and the bf16 packing of element e
+                auto finish = [&](int e, float p, float d) {
+                    const float t = p * d;
+                    if (e & 1) {
+                        pw[e >> 1] = pack_bf16x2(pe, p);
+                        tw[e >> 1] = pack_bf16x2(te, t);
+                        asm volatile("" : "+v"(pw[e >> 1]), "+v"(tw[e >> 1]));
+                    } else {
+                        pe = p;
+                        te = t;
+                    }
+                };
                 constexpr int kDV = 2 * C::kMT;            // dV MFMAs (and as many dK MFMAs)
                 constexpr int kSlots = 4 * kDV > 32 ? 4 * kDV : 32;
 #pragma unroll
                 for (int k = 0; k < kSlots; ++k) {
                     if (k == kDV) {
-                        read_rows(sn, 0, qr, kH, kH);
-                        read_rows(sn, 1, dr, kH, kH);
+                        uint32_t ra[4];
+                        rows_addr(sn, ra);
+                        read_rows(ra, 0, qr, kH, kH);
+                        read_rows(ra, 1, dr, kH, kH);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     if (k == 2 * kDV) {
                         // dt/qt of st-1 consumed: read stage st's transposed fragments for st+1
-                        read_cols(st, 1, dt);
-                        read_cols(st, 0, qt);
+                        read_cols(st, dt, qt);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     if (k < 2 * kDV) {
@@ -738,19 +798,12 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                         if ((j & 1) == 0) Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qr[ks]), __builtin_bit_cast(bf16x8, kf[ks]), Sn, 0, 0, 0);
                         else Dn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dr[ks]), __builtin_bit_cast(bf16x8, vf[ks]), Dn, 0, 0, 0);
                     }
-                    if (k < 16 && (k & 3) == 0 && k + 4 < 16) read_rowvals(st, (k >> 2) + 1, l2[((k >> 2) + 1) & 1], dl[((k >> 2) + 1) & 1]);
+                    if (k < 16 && (k & 3) == 0 && k + 4 < 16) read_rowvals(rva, (k >> 2) + 1, l2[((k >> 2) + 1) & 1], dl[((k >> 2) + 1) & 1]);
                     if (k < 16) {
                         const int i = k, jb = (i >> 2) & 1;
+                        const float d = Dc[i] - dl[jb][i & 3];
                         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[i], c2, -l2[jb][i & 3]));
-                        const float t = p * (Dc[i] - dl[jb][i & 3]);
-                        if (i & 1) {
-                            pw[i >> 1] = pack_bf16x2(pe, p);
-                            tw[i >> 1] = pack_bf16x2(te, t);
-                            asm volatile("" : "+v"(pw[i >> 1]), "+v"(tw[i >> 1]));
-                        } else {
-                            pe = p;
-                            te = t;
-                        }
+                        finish(i, p, d);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -841,8 +894,9 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
 // =============================================================================================
 // Row values and the combined kernel
 // =============================================================================================
-// lse in log2 units and delta = rowsum(dO * O) of every (row, head), into the head-major
-// [2][H][rows] workspace that the dK/dV stages load 32 rows at a time.  Sixteen lanes per (row,
+// lse in log2 units and delta = rowsum(dO * O) of every (row, head), as adjacent pairs in the
+// head-major [H][rows][2] workspace, so that the 32 rows of a dK/dV stage are 256 contiguous
+// bytes (one 4-byte direct load per lane).  Sixteen lanes per (row,
 // head): lane c takes the 8 elements of 16-byte chunk c (consecutive lanes read consecutive
 // chunks, so a wave's loads are contiguous), then a butterfly over the 16 lanes sums them.
 template <int D, int MODE>
@@ -882,8 +936,8 @@ __global__ __launch_bounds__(256) void bwd_rowvals_kernel(BwdArgs args) {
             const int head = (int)(t - row * H);
             // a row that saw no key at all (lse = -inf) gets +inf, so that every P of it is 0
             const float l = args.lse[t];
-            args.rowvals[(int64_t)head * rows + row] = l == -INFINITY ? INFINITY : l * kLog2e;
-            args.rowvals[((int64_t)H + head) * rows + row] = part;
+            const f32x2 w = {l == -INFINITY ? INFINITY : l * kLog2e, part};
+            *(f32x2*)(args.rowvals + 2 * ((int64_t)head * rows + row)) = w;
         }
     }
 }

@@ -78,8 +78,8 @@ struct BwdArgs {
     int32_t H, Hkv;
     float scale;
     float scale_log2;
-    float* rowvals;         // [2][H][T] workspace written by the row-values pass: lse * log2(e)
-                            // and delta = rowsum(dO * out), rows of one head contiguous
+    float* rowvals;         // [H][T][2] workspace written by the row-values pass: pairs of
+                            // lse * log2(e) and delta = rowsum(dO * out), rows of one head contiguous
     uint16_t* dq;           // varlen: bf16 [T][H][D]
     uint16_t* dk;           // varlen: bf16 [T][Hkv][D]
     uint16_t* dv;
