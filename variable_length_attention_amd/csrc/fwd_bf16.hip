@@ -74,6 +74,7 @@ template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     using C = Cfg<D>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][C::kTileBytes];
+    const uint32_t ring0 = lds_addr(smem);                 // LDS byte address of ring buffer 0
     __shared__ __attribute__((aligned(1024))) unsigned char obuf[kWaves][32 * kStageRowBytes];
     // a wave's Q staging tile (64 rows) fits a ring buffer and two output tiles
     static_assert(kRowsPerWave * C::kRowBytes <= C::kTileBytes && kRowsPerWave * C::kRowBytes <= 2 * 32 * kStageRowBytes,
@@ -301,15 +302,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
         };
 
-        // LDS base of unit u's rows in the K (kv = 0) or V (kv = 1) ring buffer: uniform
-        auto unit_base = [&](int u, int kv) {
-            return (uint32_t)__builtin_amdgcn_readfirstlane(
-                (int)(lds_addr(smem[(u >> 1) % kStages][kv]) + (u & 1) * 32 * C::kRowBytes));
+        // LDS base of a unit's 32 rows: half h of the K (kv = 0) or V (kv = 1) tile of ring
+        // buffer buf (uniform)
+        auto unit_base = [&](int buf, int h, int kv) {
+            return ring0 + (uint32_t)buf * (2 * C::kTileBytes) + (uint32_t)kv * C::kTileBytes +
+                   (uint32_t)h * (32 * C::kRowBytes);
         };
-        // K fragments of unit u (A operand of the score product): 4 lane addresses, the
-        // k-steps differ by immediate offsets
-        auto read_k = [&](int u, u32x4 (&kf)[C::kKS]) {
-            const uint32_t kb = unit_base(u, 0);
+        // ring buffers of the current unit's stage and of the next stage load (stage st lives
+        // in buffer st mod kStages), advanced by the steps instead of divided
+        int cbuf = 0, lbuf = 2;
+        // K fragments of the unit in half h of buffer buf (A operand of the score product): 4
+        // lane addresses, the k-steps differ by immediate offsets
+        auto read_k = [&](int buf, int h, u32x4 (&kf)[C::kKS]) {
+            const uint32_t kb = unit_base(buf, h, 0);
             uint32_t a[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) a[j] = lds_add(kb, kofs[j]);
@@ -320,8 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // V^T fragments of unit u (A operand of the value product), transposing LDS reads: for
         // k-step ks2 and D tile mt, lane l receives 8 values of column mt*32 + l%32 from the
         // unit's rows 16 ks2 + 8 (i/4) + 4 (l/32) + i%4 (the accumulator row order)
-        auto read_v = [&](int u, bf16x8 (&vf)[2][C::kMT]) {
-            const uint32_t vb = unit_base(u, 1);
+        auto read_v = [&](int buf, int h, bf16x8 (&vf)[2][C::kMT]) {
+            const uint32_t vb = unit_base(buf, h, 1);
             const uint32_t a[2] = {lds_add(vb, vofs[0]), lds_add(vb, vofs[1])};
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
@@ -405,7 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             __syncthreads();
             const int st = (u + 3) >> 1;
-            if (st < n_stages) load_stage(st, st % kStages);
+            if (st < n_stages) load_stage(st, lbuf);
+            lbuf = lbuf == kStages - 1 ? 0 : lbuf + 1;
         };
         auto stage_prologue = [&]() {
             if (n_units > 0) {
@@ -613,7 +619,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                         bf16x8 (&Pc)[kNT][2]) {
             if (odd) stage_turn(u);
             u32x4 kf[C::kKS];
-            read_k(u + 1, kf);
+            // unit u + 1: the second half of this stage (u even) or the first of the next (u odd)
+            const int nbuf = cbuf == kStages - 1 ? 0 : cbuf + 1;
+            read_k(odd ? nbuf : cbuf, odd ? 0 : 1, kf);
             __builtin_amdgcn_sched_barrier(0);
             // 32 slots: one MFMA (value-product MFMAs, then score-product MFMAs) and the softmax
             // work of one score element (against the current reference: no dependency on this
@@ -634,7 +642,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
             for (int k = 0; k < kSlots; ++k) {
                 if (k == kPV) {
-                    read_v(u, vf);
+                    read_v(cbuf, odd ? 1 : 0, vf);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (k >= kPV + kQK) {
@@ -671,6 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
             fix_rescale(Sc, Pc, ls, lb);
             if (u + 1 < n_units && !unit_full(u + 1)) apply_mask(u + 1, Sn);
+            if (odd) cbuf = nbuf;
         };
         if (n_units > 0) {
             f32x16 SA[kNT], SB[kNT];
@@ -683,10 +692,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             read_q();
             {
                 u32x4 kf[C::kKS];
-                read_k(0, kf);
+                read_k(0, 0, kf);
                 score(kf, SA);
             }
-            read_v(0, vf);   // multiplied by the zero P of unit -1
+            read_v(0, 0, vf);   // multiplied by the zero P of unit -1
             if (!unit_full(0)) apply_mask(0, SA);
             int u = 0;
             for (; u + 1 < n_units; u += 2) {
