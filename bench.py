@@ -339,8 +339,21 @@ def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
 def run_sample(torch, ops, synth, name: str, launches: int) -> dict:
     """`launches` launches of one named workload with nothing else around them: the command a
     counter profile of one kernel runs (slice_fwd, long_fwd, short_fwd, ring_chunk, merge,
-    slice_bwd, single_bwd)."""
-    if name in ("ring_chunk", "merge"):
+    slice_bwd, single_bwd, chunk_bwd_past, chunk_bwd_diag)."""
+    if name in ("chunk_bwd_past", "chunk_bwd_diag"):
+        # one backward ring step of the 128K share: chunk 0 (wholly in the past of the slice)
+        # or chunk 15 (the slice's own diagonal chunk), into fp32 accumulators
+        w = synth.ring_chunks_128k()
+        q, k, v = (t.cuda() for t in synth.ring_tensors(w))
+        o, lse, do = (t.cuda() for t in synth.ring_bwd_tensors(w))
+        L = w.chunk_len
+        c = 0 if name == "chunk_bwd_past" else w.n_chunks - 1
+        kc, vc = k[c * L:(c + 1) * L], v[c * L:(c + 1) * L]
+        dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+        dk = torch.zeros((L, w.Hkv, w.D), dtype=torch.float32, device="cuda")
+        dv = torch.zeros_like(dk)
+        fn = lambda: ops.hdp_attn_chunk_bwd(q, kc, vc, w.q_offset, c * L, o, lse, do, dq, dk, dv, True, w.scale)
+    elif name in ("ring_chunk", "merge"):
         w = synth.ring_chunks_128k()
         q, k, v = (t.cuda() for t in synth.ring_tensors(w))
         L = w.chunk_len
@@ -379,7 +392,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sample", default=None,
                     help="only time --steps launches of one workload (slice_fwd, long_fwd, short_fwd, "
-                         "ring_chunk, merge, slice_bwd, single_bwd), for counter profiles")
+                         "ring_chunk, merge, slice_bwd, single_bwd, chunk_bwd_past, chunk_bwd_diag), for "
+                         "counter profiles")
     ap.add_argument("--cu-timeline", action="store_true",
                     help="print only the per-workgroup (one per CU) finish-time summary of the forward "
                          "on the 8K slice and the 32K micro-batches")
