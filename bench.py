@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector (the fp32 path's roofline)
 NOMINAL_MHZ = 2400.0          # the clock the bf16 peak is quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_packed_slice_8k.json")
 # the forward kernel's sources: counters taken on another version of them do not apply
@@ -266,6 +267,20 @@ def detail_rows(torch, ops, synth):
         fl = sum(ops.hdp_seq_flops(s, w.H, w.D) for s in w.lengths)
         out[w.name] = {"n_seq": len(w.lengths), "GFLOP": fl / 1e9, "kernel_us": ms * 1e3,
                        "TFLOP/s": fl / (ms * 1e-3) / 1e12, "launch": us_stats(t_m)}
+    # the tiny fp32 pack (4 sequences, 256 tokens, H = 4, D = 64): a VALU kernel, one lane per
+    # row, launch-bound by design; its roofline is the fp32 vector peak
+    w = synth.tiny_fp32_pack()
+    qq, kk, vv = (t.cuda() for t in synth.varlen_tensors(w))
+    cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
+    o = torch.empty_like(qq)
+    lse = torch.empty((qq.shape[0], w.H), dtype=torch.float32, device="cuda")
+    t_t = timed_floor(lambda: ops.hdp_attn_varlen_fwd_f32(qq, kk, vv, cu, w.scale, out=o, lse=lse), torch,
+                      min_launches=200)
+    fl = sum(ops.hdp_seq_flops(s, w.H, w.D) for s in w.lengths)
+    out[w.name] = {"n_seq": len(w.lengths), "GFLOP": fl / 1e9, "kernel_us": t_t["mean_ms"] * 1e3,
+                   "fp32_tflops": fl / (t_t["mean_ms"] * 1e-3) / 1e12,
+                   "frac_fp32_vector_peak": fl / (t_t["mean_ms"] * 1e-3) / 1e12 / PEAK_FP32_VECTOR_TFLOPS,
+                   "launch": us_stats(t_t)}
     # every throughput also as a fraction of its roofline: TFLOP/s against the bf16 MFMA peak,
     # GB/s against HBM
     def add_fracs(row):

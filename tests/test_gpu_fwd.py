@@ -42,8 +42,26 @@ def test_tiny_fp32_pack_full():
     qg, kg, vg = to_gpu(q, k, v)
     out, lse = ops.hdp_attn_varlen_fwd_f32(qg, kg, vg, torch.from_numpy(cu).cuda(), w.scale)
     torch.cuda.synchronize()
-    assert max_abs(out, ro) <= TOL_F32
-    assert max_abs(lse, rl) <= TOL_F32
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print("%s: all %d rows, max|dout|=%.3g max|dlse|=%.3g" % (w.name, int(cu[-1]), e_out, e_lse))
+    assert e_out <= TOL_F32
+    assert e_lse <= TOL_F32
+
+
+@pytest.mark.parametrize("lengths,H,Hkv,D", [([1, 5, 37, 0, 260, 33], 8, 2, 128),
+                                             ([3, 100, 64, 131], 6, 3, 64)])
+def test_fp32_ragged_pack_full(lengths, H, Hkv, D):
+    # grouped heads, empty and single-token sequences, rows past the 32 that one pass of the
+    # kernel's waves covers, and key counts that are not multiples of its 4-key blocks
+    w, q, k, v, cu = varlen_case(lengths, H, Hkv, D, 23, dtype="f32")
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    qg, kg, vg = to_gpu(q, k, v)
+    out, lse = ops.hdp_attn_varlen_fwd_f32(qg, kg, vg, torch.from_numpy(cu).cuda(), w.scale)
+    torch.cuda.synchronize()
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print("fp32 lengths=%s H=%d Hkv=%d D=%d max|dout|=%.3g max|dlse|=%.3g" % (lengths, H, Hkv, D, e_out, e_lse))
+    assert e_out <= TOL_F32
+    assert e_lse <= TOL_F32
 
 
 RAGGED = [1, 17, 64, 65, 127, 128, 129, 300, 0, 513, 31]

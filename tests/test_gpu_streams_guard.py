@@ -108,6 +108,14 @@ def test_outputs_never_write_outside_their_buffers(D):
         g.check("varlen bwd " + n)
     ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
     assert max_abs(out.t, ro) <= TOL_BF16_OUT
+    # the fp32 form on the same pack
+    qf, kf, vf = (t.float().cuda() for t in (q, k, v))
+    out32 = Guarded((T, H, D), torch.float32)
+    lse32 = Guarded((T, H), torch.float32)
+    ops.hdp_attn_varlen_fwd_f32(qf, kf, vf, cug, w.scale, out=out32.t, lse=lse32.t)
+    out32.check("fp32 fwd out")
+    lse32.check("fp32 fwd lse")
+    assert max_abs(out32.t, ro) <= 1e-5
 
     # ring step, its merge and its backward on ragged sizes
     Lq, Lk, q_off, kv_off = 77, 45, 60, 20

@@ -612,9 +612,14 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
             // all waves count the same memory ops.  The chunk form (fp32 read-modify-write
             // epilogue) keeps the per-load path: with both paths it no longer fits its registers.
             if (MODE == 0 && r0 + kUnit <= s) {
-                const int64_t sofs = (base + r0) * q_stride + (int64_t)head * D;
-                if constexpr (kBPW == 1) lds_dma16_pairs<1>(args.q + sofs, args.dout + sofs, voffq, lq, lq + kTile);
-                else lds_dma16_tiles<kBPW>(args.q + sofs, args.dout + sofs, voffq, lq, lq + kTile);
+                // the (row, head) index stays below T x H <= INT32_MAX (checked on the host), so
+                // it is a 32-bit product; only the byte offset is 64-bit
+                const uint32_t qi = (uint32_t)(((int)base + r0) * H + head);
+                const uint64_t qb = (uint64_t)qi * (uint64_t)(D * 2);
+                const unsigned char* sq = (const unsigned char*)args.q + qb;
+                const unsigned char* sd = (const unsigned char*)args.dout + qb;
+                if constexpr (kBPW == 1) lds_dma16_pairs<1>(sq, sd, voffq, lq, lq + kTile);
+                else lds_dma16_tiles<kBPW>(sq, sd, voffq, lq, lq + kTile);
                 lds_dma4_s(args.rowvals + 2 * ((int64_t)head * Trv + base + r0), 4u * lane, lrv);
             } else {
                 // the stage at the sequence's end: rows clamped to its last row
