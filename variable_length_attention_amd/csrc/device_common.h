@@ -206,6 +206,27 @@ __device__ inline void lds_dma16_tiles(const void* sbase0, const void* sbase1, c
             : "memory");
     }
 }
+// The pieces of lds_dma16_tiles issued one at a time, so that a stage's loads can be spread
+// between other instructions: dma_tile_begin saves M0 and points it at a tile's LDS base,
+// dma_tile_load issues block I of the tile (global sbase + voffb + 1024 I, LDS M0 + 1024 I +
+// 16 * lane; voffb as for lds_dma16_tiles), dma_tile_switch points M0 at the next tile and
+// dma_tile_end restores M0.  Between begin and end nothing else may write M0 (the callers' code
+// there uses no instruction that does: checked in the generated code).
+__device__ inline uint32_t dma_tile_begin(uint32_t lds) {
+    uint32_t m0_saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0" : "=&s"(m0_saved) : "s"(lds) : "memory");
+    return m0_saved;
+}
+__device__ inline void dma_tile_switch(uint32_t lds) {
+    asm volatile("s_nop 0\n\ts_mov_b32 m0, %0\n\ts_nop 0" :: "s"(lds) : "memory");
+}
+template <int I>
+__device__ inline void dma_tile_load(const void* sbase, uint32_t voffb) {
+    asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" :: "v"(voffb), "s"(sbase), "n"(1024 * I) : "memory");
+}
+__device__ inline void dma_tile_end(uint32_t m0_saved) {
+    asm volatile("s_nop 0\n\ts_mov_b32 m0, %0" :: "s"(m0_saved) : "memory");
+}
 // One direct load of 4 bytes per lane in the scalar-base form (sbase + voff -> lds + 4 * lane).
 __device__ inline void lds_dma4_s(const void* sbase, uint32_t voff, uint32_t lds) {
     uint32_t m0_saved;

@@ -405,13 +405,46 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
         };
         // stage ring (called at odd u only): stage (u+3)/2 goes into the buffer of stage (u-3)/2 (last read
-        // in iteration u-1 or earlier); stage (u+1)/2, issued at u-2, must have landed.
+        // in iteration u-1 or earlier); stage (u+1)/2, issued at u-2, must have landed.  A whole
+        // stage's loads are not issued here but spread over the value-product slots of step u
+        // (spread_k / spread_v / spread_lk / spread_lv): issued back to back right after the
+        // barrier, the four waves' loads queue up at once and hold each wave for hundreds of
+        // cycles.  The last stage of an item (rows clamped) is loaded here.
+        bool spread = false;
+        const uint16_t* spread_k = args.k;
+        const uint16_t* spread_v = args.v;
+        uint32_t spread_lk = 0, spread_lv = 0;
         auto stage_turn = [&](int u) {
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             __syncthreads();
             const int st = (u + 3) >> 1;
-            if (st < n_stages) load_stage(st, lbuf);
+            spread = st < n_stages && st * kStage + kStage <= sk;
+            if (spread) {
+                const int64_t sofs = (kbase + st * kStage) * kv_stride + (int64_t)g * D;
+                spread_k = args.k + sofs;
+                spread_v = args.v + sofs;
+                spread_lk = ring0 + (uint32_t)lbuf * (2 * C::kTileBytes) + wave * C::kBlocksPerWave * 1024;
+                spread_lv = spread_lk + C::kTileBytes;
+            } else if (st < n_stages) {
+                load_stage(st, lbuf);
+            }
             lbuf = lbuf == kStages - 1 ? 0 : lbuf + 1;
+        };
+        // block i of the spread stage's K tile (i < kBlocksPerWave) or V tile, with the M0
+        // handling around the first and last load
+        uint32_t spread_m0 = 0;
+        auto spread_load = [&](int i) {
+            constexpr int NB = C::kBlocksPerWave;
+            if (i == 0) spread_m0 = dma_tile_begin(spread_lk);
+            if (i == NB) dma_tile_switch(spread_lv);
+            const uint16_t* base = i < NB ? spread_k : spread_v;
+            switch (i % NB) {
+                case 0: dma_tile_load<0>(base, gofs[0]); break;
+                case 1: dma_tile_load<1>(base, gofs[1]); break;
+                case 2: if constexpr (NB > 2) dma_tile_load<2>(base, gofs[NB > 2 ? 2 : 0]); break;
+                default: if constexpr (NB > 3) dma_tile_load<3>(base, gofs[NB > 3 ? 3 : 0]); break;
+            }
+            if (i == 2 * NB - 1) dma_tile_end(spread_m0);
         };
         auto stage_prologue = [&]() {
             if (n_units > 0) {
@@ -645,6 +678,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                     read_v(cbuf, odd ? 1 : 0, vf);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if (odd && (k & 1) == 0 && k / 2 < 2 * C::kBlocksPerWave && spread) spread_load(k / 2);
                 if (k >= kPV + kQK) {
                     // (D = 64: more score elements than MFMAs)
                 } else if (k < kPV) {
