@@ -196,7 +196,7 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
         if (lane == 0) k = atomicAdd(&counters[queue * kQueueStride], 1);
         return k;
     };
-    if (wave == 0) publish(__shfl(pop(), 0), 0);
+    if (wave == 0) publish(__builtin_amdgcn_readfirstlane(pop()), 0);
     __syncthreads();
 
     for (int it = 0;; ++it) {
@@ -434,7 +434,7 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
                     }
             }
         }
-        if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
+        if (wave == 0) publish(__builtin_amdgcn_readfirstlane(k_next), slot ^ 1);
         __syncthreads();
     }
 }
@@ -554,7 +554,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
         if (lane == 0) k = atomicAdd(&counters[queue * kQueueStride], 1);
         return k;
     };
-    if (wave == 0) publish(__shfl(pop(), 0), 0);
+    if (wave == 0) publish(__builtin_amdgcn_readfirstlane(pop()), 0);
     __syncthreads();
 
     for (int it = 0;; ++it) {
@@ -891,7 +891,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                 }
             }
         }
-        if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
+        if (wave == 0) publish(__builtin_amdgcn_readfirstlane(k_next), slot ^ 1);
         __syncthreads();
     }
 }

@@ -152,6 +152,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     // run at the same speed, and otherwise the launch waits for the slowest one's queue.
     int src_q = queue;
     int stolen = 0;
+    // the atomic's result is in lane 0; callers take it with readfirstlane, so the decode that
+    // follows is scalar code (a lane shuffle would leave it in a vector register)
     auto pop = [&]() {
         int k = 0;
         if (lane == 0) k = atomicAdd(&args.counters[src_q * kQueueStride], 1);
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         while (k >= plan.total && stolen < nq_queues - 1) {
             ++stolen;
             src_q = (queue + stolen) % nq_queues;
-            k = __shfl(pop(), 0);
+            k = __builtin_amdgcn_readfirstlane(pop());
         }
         int a = 0, len = 0, hbq = 0, c = 0;
         bool ok = k < plan.total;
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             s_item[4 * slot + 3] = c - 1;                 // query tile group: cost grows with it
         }
     };
-    if (wave == 0) publish(__shfl(pop(), 0), 0);
+    if (wave == 0) publish(__builtin_amdgcn_readfirstlane(pop()), 0);
     __syncthreads();
 
     int it = 0;                                  // items processed
@@ -753,7 +755,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // is taken here before any wave overwrites a tile that another may still be reading.
         if (n_units == 1) __syncthreads();
         store_rows(o, m, l);
-        if (wave == 0) publish(__shfl(k_next, 0), slot ^ 1);
+        if (wave == 0) publish(__builtin_amdgcn_readfirstlane(k_next), slot ^ 1);
         __syncthreads();
     }
 
