@@ -273,19 +273,17 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks) f[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
         };
-        auto read_cols = [&](uint32_t ub, int kv, bf16x8 (&f)[2][C::kMT]) {
-            const uint32_t b = ub + kv * kTile;
-            const uint32_t a[2] = {lds_add(b, tofs[0]), lds_add(b, tofs[1])};
-#pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-                for (int mt = 0; mt < C::kMT; ++mt) {
-                    const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
-                    f[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
-                    f[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
-                }
+        // transposed K fragment (ks2, mt) of the unit at ub; a = per-lane column bases (cols_addr)
+        auto cols_addr = [&](uint32_t ub, uint32_t (&a)[2]) {
+            a[0] = lds_add(ub, tofs[0]);
+            a[1] = lds_add(ub, tofs[1]);
+        };
+        auto read_col = [&](const uint32_t (&a)[2], int ks2, int mt, bf16x8& f) {
+            const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
+            f.lo = __builtin_bit_cast(bf16x4, lo);
+            f.hi = __builtin_bit_cast(bf16x4, hi);
         };
         // key j of the item is visible to this lane's row iff j <= lim (and the row exists);
         // invisible elements of a unit get S = -inf, so P = 0 and dS = 0
@@ -328,13 +326,17 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             constexpr int kDQ = 2 * C::kMT;              // dQ MFMAs
             constexpr int kSD = 2 * C::kKS;              // S and dP MFMAs
             constexpr int kSlots = kDQ + kSD > 16 ? kDQ + kSD : 16;
-            uint32_t tw[8];
+            static_assert(kSD == 2 * kDQ, "a transposed fragment every second S/dP slot");
+            uint32_t tw[8], ca[2];
             float te = 0.f;
 #pragma unroll
             for (int k = 0; k < kSlots; ++k) {
-                if (k == kDQ) {
-                    read_cols(unit_base(cbuf, odd), 0, kt);   // K^T of unit u, for the next step
-                    __builtin_amdgcn_sched_barrier(0);
+                if (k >= kDQ && k < kDQ + kSD && ((k - kDQ) & 1) == 0) {
+                    // K^T of unit u for the next step (its dQ products of u - 1 are issued), one
+                    // fragment every second S/dP slot in the order the next step uses them
+                    const int f = (k - kDQ) >> 1;
+                    if (f == 0) cols_addr(unit_base(cbuf, odd), ca);
+                    read_col(ca, f / C::kMT, f % C::kMT, kt[f / C::kMT][f % C::kMT]);
                 }
                 if (k < kDQ) {
                     const int ks2 = k / C::kMT, mt = k % C::kMT;
@@ -650,22 +652,18 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
         };
         // B-operand transposed fragments: for k-step ks2 and D tile mt, lane l receives column
         // mt*32 + l%32 of rows 16 ks2 + 8 (i/4) + 4 (l/32) + i%4 (the accumulator row order)
-        auto read_cols = [&](int st, bf16x8 (&fd)[2][C::kMT], bf16x8 (&fq)[2][C::kMT]) {
+        // (a[0], a[1] = per-lane column bases of the stage, from cols_addr; which = 1: dO, 0: Q)
+        auto cols_addr = [&](int st, uint32_t (&a)[2]) {
             const uint32_t b = stage_lds(st);
-            const uint32_t a[2] = {lds_add(b, tofs[0]), lds_add(b, tofs[1])};
-#pragma unroll
-            for (int which = 1; which >= 0; --which)
-#pragma unroll
-                for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-                    for (int mt = 0; mt < C::kMT; ++mt) {
-                        const uint32_t p0 = a[mt & 1] + which * kTile + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
-                        bf16x8& f = which ? fd[ks2][mt] : fq[ks2][mt];
-                        f.lo = __builtin_bit_cast(bf16x4, lo);
-                        f.hi = __builtin_bit_cast(bf16x4, hi);
-                    }
+            a[0] = lds_add(b, tofs[0]);
+            a[1] = lds_add(b, tofs[1]);
+        };
+        auto read_col = [&](const uint32_t (&a)[2], int which, int ks2, int mt, bf16x8& f) {
+            const uint32_t p0 = a[mt & 1] + which * kTile + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
+            f.lo = __builtin_bit_cast(bf16x4, lo);
+            f.hi = __builtin_bit_cast(bf16x4, hi);
         };
         // lse2 and delta of the lane's accumulator rows 8*j + 4*half + (0..3) (elements 4j..4j+3):
         // four (lse2, delta) pairs at rva + 64 j
@@ -778,6 +776,8 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                 };
                 constexpr int kDV = 2 * C::kMT;            // dV MFMAs (and as many dK MFMAs)
                 constexpr int kSlots = 4 * kDV > 32 ? 4 * kDV : 32;
+                static_assert(2 * kDV <= 2 * C::kKS, "one transposed fragment per S/dP slot");
+                uint32_t ca[2];
 #pragma unroll
                 for (int k = 0; k < kSlots; ++k) {
                     if (k == kDV) {
@@ -787,10 +787,13 @@ __device__ __attribute__((always_inline)) inline void dkdv_body(const BwdArgs& a
                         read_rows(ra, 1, dr, kH, kH);
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                    if (k == 2 * kDV) {
-                        // dt/qt of st-1 consumed: read stage st's transposed fragments for st+1
-                        read_cols(st, dt, qt);
-                        __builtin_amdgcn_sched_barrier(0);
+                    if (k >= 2 * kDV && k < 4 * kDV) {
+                        // dt/qt of st-1 consumed: stage st's transposed fragments for st+1, one
+                        // per S/dP slot in the order the next step's dV/dK products use them
+                        const int j = k - 2 * kDV, f = j >> 1, ks2 = f / C::kMT, mt = f % C::kMT;
+                        if (j == 0) cols_addr(st, ca);
+                        if (j & 1) read_col(ca, 0, ks2, mt, qt[ks2][mt]);
+                        else read_col(ca, 1, ks2, mt, dt[ks2][mt]);
                     }
                     if (k < 2 * kDV) {
                         const int j = k >> 1, ks2 = j / C::kMT, mt = j % C::kMT;
