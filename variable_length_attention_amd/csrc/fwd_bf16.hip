@@ -315,11 +315,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         int cbuf = 0, lbuf = 2;
         // K fragments of the unit in half h of buffer buf (A operand of the score product): 4
         // lane addresses, the k-steps differ by immediate offsets
-        auto read_k = [&](int buf, int h, u32x4 (&kf)[C::kKS]) {
+        auto k_addr = [&](int buf, int h, uint32_t (&a)[4]) {
             const uint32_t kb = unit_base(buf, h, 0);
-            uint32_t a[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) a[j] = lds_add(kb, kofs[j]);
+        };
+        auto read_k = [&](int buf, int h, u32x4 (&kf)[C::kKS]) {
+            uint32_t a[4];
+            k_addr(buf, h, a);
 #pragma unroll
             for (int ks = 0; ks < C::kKS; ++ks)
                 kf[ks] = *(const lds_u32x4*)(uintptr_t)(a[ks & 3] + 128 * (ks >> 2));
@@ -327,19 +330,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // V^T fragments of unit u (A operand of the value product), transposing LDS reads: for
         // k-step ks2 and D tile mt, lane l receives 8 values of column mt*32 + l%32 from the
         // unit's rows 16 ks2 + 8 (i/4) + 4 (l/32) + i%4 (the accumulator row order)
-        auto read_v = [&](int buf, int h, bf16x8 (&vf)[2][C::kMT]) {
+        // (v_addr: the two per-lane column bases of the unit; read_vh: half hi of fragment
+        // (ks2, mt); read_v: every fragment)
+        auto v_addr = [&](int buf, int h, uint32_t (&a)[2]) {
             const uint32_t vb = unit_base(buf, h, 1);
-            const uint32_t a[2] = {lds_add(vb, vofs[0]), lds_add(vb, vofs[1])};
+            a[0] = lds_add(vb, vofs[0]);
+            a[1] = lds_add(vb, vofs[1]);
+        };
+        auto read_vh = [&](const uint32_t (&a)[2], int ks2, int mt, int hi, bf16x8& f) {
+            const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes + hi * 8 * C::kRowBytes;
+            const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
+            if (hi) f.hi = __builtin_bit_cast(bf16x4, x);
+            else f.lo = __builtin_bit_cast(bf16x4, x);
+        };
+        auto read_v = [&](int buf, int h, bf16x8 (&vf)[2][C::kMT]) {
+            uint32_t a[2];
+            v_addr(buf, h, a);
 #pragma unroll
             for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
                 for (int mt = 0; mt < C::kMT; ++mt) {
-                    const uint32_t p0 = a[mt & 1] + 128 * (mt >> 1) + 16 * ks2 * C::kRowBytes;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)p0);
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(uintptr_t)(p0 + 8 * C::kRowBytes));
-                    vf[ks2][mt].lo = __builtin_bit_cast(bf16x4, lo);
-                    vf[ks2][mt].hi = __builtin_bit_cast(bf16x4, hi);
+                    read_vh(a, ks2, mt, 0, vf[ks2][mt]);
+                    read_vh(a, ks2, mt, 1, vf[ks2][mt]);
                 }
         };
         // S^T (32 keys x 64 rows) = K Q^T
@@ -656,7 +668,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             u32x4 kf[C::kKS];
             // unit u + 1: the second half of this stage (u even) or the first of the next (u odd)
             const int nbuf = cbuf == kStages - 1 ? 0 : cbuf + 1;
-            read_k(odd ? nbuf : cbuf, odd ? 0 : 1, kf);
+            uint32_t ka[4];
+            k_addr(odd ? nbuf : cbuf, odd ? 0 : 1, ka);
             __builtin_amdgcn_sched_barrier(0);
             // 32 slots: one MFMA (value-product MFMAs, then score-product MFMAs) and the softmax
             // work of one score element (against the current reference: no dependency on this
@@ -668,6 +681,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             float ls[kNT], lb[kNT], p1 = 0.f, p2 = 0.f;       // P of the two previous elements
             const float (&mb)[kNT] = mref;
             uint32_t pw[kNT][8];                                   // P as bf16 pairs
+            uint32_t va[2];
+            constexpr int kVR = 4 * C::kMT;                        // transposing V reads per unit
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
                 ls[nt] = 0.f;
@@ -676,9 +691,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
 #pragma unroll
             for (int k = 0; k < kSlots; ++k) {
-                if (k == kPV) {
-                    read_v(cbuf, odd ? 1 : 0, vf);
-                    __builtin_amdgcn_sched_barrier(0);
+                if (k >= kPV && k < kPV + kVR) {
+                    // V^T of unit u for the next step (its value products of u - 1 are issued),
+                    // one read per score-product slot in the order the next step uses them
+                    const int j = k - kPV, f = j >> 1;
+                    if (j == 0) v_addr(cbuf, odd ? 1 : 0, va);
+                    read_vh(va, f / C::kMT, f % C::kMT, j & 1, vf[f / C::kMT][f % C::kMT]);
+                }
+                if (k < kPV && (k % (kPV / C::kKS)) == 0) {
+                    // K of unit u + 1, spread over the value-product slots
+                    const int ks = k / (kPV / C::kKS);
+                    kf[ks] = *(const lds_u32x4*)(uintptr_t)(ka[ks & 3] + 128 * (ks >> 2));
                 }
                 if (odd && (k & 1) == 0 && k / 2 < 2 * C::kBlocksPerWave && spread) spread_load(k / 2);
                 if (k >= kPV + kQK) {
