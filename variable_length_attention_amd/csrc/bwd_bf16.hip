@@ -320,8 +320,9 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             // the next (u odd); past the end, unit u again (a harmless re-read)
             const int nbuf = cbuf == kStages - 1 ? 0 : cbuf + 1;
             const uint32_t un_base = u + 1 >= n_units ? unit_base(cbuf, odd) : odd ? unit_base(nbuf, 0) : unit_base(cbuf, 1);
-            read_rows(un_base, 0, kf);
-            read_rows(un_base, 1, vf);
+            uint32_t ra[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ra[j] = lds_add(un_base, rofs[j]);
             __builtin_amdgcn_sched_barrier(0);
             constexpr int kDQ = 2 * C::kMT;              // dQ MFMAs
             constexpr int kSD = 2 * C::kKS;              // S and dP MFMAs
@@ -331,6 +332,17 @@ __device__ __attribute__((always_inline)) inline void dq_body(const BwdArgs& arg
             float te = 0.f;
 #pragma unroll
             for (int k = 0; k < kSlots; ++k) {
+                if (k < kDQ) {
+                    // K and V rows of unit u + 1, two reads per dQ slot in the order the S and
+                    // dP products use them
+#pragma unroll
+                    for (int r = 0; r < kSD / kDQ; ++r) {
+                        const int j = k * (kSD / kDQ) + r, ks = j >> 1;
+                        const uint32_t a = ra[ks & 3] + (j & 1) * kTile + 128 * (ks >> 2);
+                        if (j & 1) vf[ks] = *(const lds_u32x4*)(uintptr_t)a;
+                        else kf[ks] = *(const lds_u32x4*)(uintptr_t)a;
+                    }
+                }
                 if (k >= kDQ && k < kDQ + kSD && ((k - kDQ) & 1) == 0) {
                     // K^T of unit u for the next step (its dQ products of u - 1 are issued), one
                     // fragment every second S/dP slot in the order the next step uses them
