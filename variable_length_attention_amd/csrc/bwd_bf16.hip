@@ -109,9 +109,9 @@ __device__ inline void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // v
 // Software-pipelined like the forward, over units of 32 keys: step u issues the dQ product of
 // unit u-1 (8 MFMAs) and the S and dP products of unit u+1 (16 MFMAs) around the elementwise
 // part of unit u (P = exp2(S c - lse2), dS = P (dP - delta), one element per slot).  K and V
-// arrive through direct global->LDS loads in a ring of three 64-key stages; K and V rows are
-// read for the products of unit u+1 at the start of a step, the transposed K fragments of
-// unit u once the dQ product of unit u-1 has been issued.
+// arrive through direct global->LDS loads in a ring of three 64-key stages; the K and V rows
+// for the products of unit u+1 are read two per dQ slot, the transposed K fragments of unit u
+// (for the next step) one per two S/dP slots, once the dQ product of unit u-1 is issued.
 template <int D>
 constexpr int dq_lds_bytes() { return kStages * 2 * kStage * Cfg<D>::kRowBytes + 8 * (int)sizeof(int); }
 
