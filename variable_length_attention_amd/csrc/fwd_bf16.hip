@@ -58,6 +58,7 @@ constexpr int kStage = 64;            // keys per LDS stage
 constexpr int kStages = 3;            // LDS ring depth
 constexpr int kStageRowBytes = 256;   // output staging tile row
 constexpr float kLazySum = 256.0f;    // rescale when a lane's unit sum of P exceeds 2^8
+constexpr int kReserveItems = 8;      // items per workgroup from which one is held in reserve
 
 template <int D>
 struct Cfg {
@@ -76,12 +77,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][C::kTileBytes];
     const uint32_t ring0 = lds_addr(smem);                 // LDS byte address of ring buffer 0
     __shared__ __attribute__((aligned(1024))) unsigned char obuf[kWaves][32 * kStageRowBytes];
-    // a wave's Q staging tile (64 rows) fits a ring buffer and two output tiles
-    static_assert(kRowsPerWave * C::kRowBytes <= C::kTileBytes && kRowsPerWave * C::kRowBytes <= 2 * 32 * kStageRowBytes,
-                  "Q staging");
-    __shared__ int s_item[8];
-    // merge mode: each output row's weight on the running accumulator, per wave
-    __shared__ float s_a1[MODE == 2 ? kWaves : 1][32];
+    // Q staging of waves 2-3 (waves 0-1 stage theirs in ring buffer 2): with its own buffer, the
+    // next item's Q can arrive while this item's output goes out through the output tiles
+    __shared__ __attribute__((aligned(1024))) unsigned char qbuf[2][kRowsPerWave * C::kRowBytes];
+    static_assert(kRowsPerWave * C::kRowBytes <= C::kTileBytes, "Q staging");
+    // item records (4 ints each): at the start two, later one, in wave 0's output tile, which is
+    // free from the end of its output stores until the next item's stores (all waves read the
+    // record at the start of that item)
+    int* const mbox = (int*)obuf[0];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
@@ -144,9 +147,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     }
 
     // ---- item queue (wave 0) ----
-    // Item k of queue src_q -> s_item[slot].  The next index is popped at the end of an item
-    // (just before its output stores, which hide the atomic's latency) and decoded once the
-    // stores are issued; two slots, because a slow wave may still read the current item's slot.
+    // Item k of queue src_q -> record slot of the mailbox.  Items are taken at the end of an
+    // item, just before its output stores (which hide the atomic's latency), and decoded once
+    // the stores are issued.  When the queue holds many items per workgroup, a workgroup knows
+    // one item ahead: it takes two items at the start and then, at the end of an item, the one
+    // after the next, so that the next item's first loads go out before this item's output
+    // stores and their latency passes under the stores.  With few items per workgroup, taking
+    // items early would unbalance the CUs (the longest-first order decides less), so each item
+    // is taken when the workgroup is about to be free and its loads go out at its start.
     // Every queue holds the same items (for its own head blocks).  A workgroup whose queue is
     // empty takes the remaining items of the other XCDs' queues in turn: the XCDs do not all
     // run at the same speed, and otherwise the launch waits for the slowest one's queue.
@@ -178,61 +186,120 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
         }
         if (lane == 0) {
-            s_item[4 * slot + 0] = ok ? a : -1;
-            s_item[4 * slot + 1] = len;
-            s_item[4 * slot + 2] = src_q + nq_queues * hbq;
-            s_item[4 * slot + 3] = c - 1;                 // query tile group: cost grows with it
+            mbox[4 * slot + 0] = ok ? a : -1;
+            mbox[4 * slot + 1] = len;
+            mbox[4 * slot + 2] = src_q + nq_queues * hbq;
+            mbox[4 * slot + 3] = c - 1;                   // query tile group: cost grows with it
         }
     };
-    if (wave == 0) publish(__builtin_amdgcn_readfirstlane(pop()), 0);
+    // query position minus key position of (row 0, key 0)
+    const int delta = MODE == 0 ? 0 : args.delta;
+    const bool causal = MODE == 0 ? true : (args.causal != 0);
+    // an item's record (uniform: scalar registers) and what follows from it
+    struct Item { int a, s_rows, hb, tg; };
+    auto read_rec = [&](int slot) {
+        return Item{__builtin_amdgcn_readfirstlane(mbox[4 * slot + 0]), __builtin_amdgcn_readfirstlane(mbox[4 * slot + 1]),
+                    __builtin_amdgcn_readfirstlane(mbox[4 * slot + 2]), __builtin_amdgcn_readfirstlane(mbox[4 * slot + 3])};
+    };
+    struct Geo { int64_t qbase, kbase; int s_rows, sk, head, g, r_lo, n_units, n_stages; };
+    auto geo = [&](const Item& x) {
+        Geo e;
+        e.qbase = x.a;
+        e.kbase = MODE == 0 ? e.qbase : 0;
+        e.s_rows = x.s_rows;
+        e.sk = MODE == 0 ? x.s_rows : args.Lk;
+        e.head = x.hb * hpw + (wave % hpw);
+        e.g = (x.hb * hpw) / G;
+        e.r_lo = x.tg * W + (wave / hpw) * kRowsPerWave;        // this wave's first row
+        // keys the workgroup visits
+        const int wg_rmax = min(x.s_rows, (x.tg + 1) * W) - 1;
+        int jmax = e.sk - 1;
+        if (causal) jmax = min(jmax, delta + wg_rmax);
+        e.n_units = (wg_rmax < 0 || jmax < 0) ? 0 : (int)(jmax / kUnit) + 1;
+        e.n_stages = (e.n_units + 1) / 2;
+        return e;
+    };
+
+    // ---- direct global -> LDS stage loads (K and V of 64 keys) into ring buffer B ----
+    // A whole stage inside the sequence takes a scalar base plus the per-lane offsets; the
+    // last stage clamps its rows to the sequence's last key.
+    auto load_stage_at = [&](int64_t kbase, int g, int sk, int st, int B) {
+        const int j0 = st * kStage;
+        // uniform base of the stage's first key row (scalar registers) + per-lane offsets
+        const int64_t sofs = (kbase + j0) * kv_stride + (int64_t)g * D;
+        const uint32_t lk = lds_addr(smem[B][0] + wave * C::kBlocksPerWave * 1024);
+        const uint32_t lv = lds_addr(smem[B][1] + wave * C::kBlocksPerWave * 1024);
+        if (j0 + kStage <= sk) {
+            lds_dma16_tiles<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, gofs, lk, lv);
+        } else {
+            uint32_t voff[C::kBlocksPerWave];
+#pragma unroll
+            for (int i = 0; i < C::kBlocksPerWave; ++i) {
+                const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
+                const int chunk = (lane % C::kChunks) ^ swz(row);
+                const int j = min(j0 + row, sk - 1) - j0;
+                voff[i] = (uint32_t)((j * kv_stride + chunk * 8) * 2);
+            }
+            lds_dma16_pairs<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, voff, lk, lv);
+        }
+    };
+    // ---- Q^T fragments in registers, loaded through LDS ----
+    // The wave's 64 query rows arrive by direct loads (16 lanes per row, so every load reads
+    // whole 256-byte rows) into a staging tile laid out like a K stage, and the fragments are
+    // then read as the K fragments are: loading the fragments straight from memory, where each
+    // lane reads its own row, takes ≈2K cycles longer per item.  The staging tiles are ring
+    // buffer 2 (waves 0-1), which the first stage turn refills, and qbuf (waves 2-3).  Rows past
+    // the sequence's end repeat its last row (their results are never stored).
+    unsigned char* const qstage = wave < 2 ? smem[2][wave] : qbuf[wave - 2];
+    auto load_q_at = [&](int64_t qbase, int head, int r_lo, int s_rows) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave / C::kRowsPerBlock; ++i) {
+            const int row = i * C::kRowsPerBlock + lane / C::kChunks;
+            const int chunk = (lane % C::kChunks) ^ swz(row);
+            const int r = min(r_lo + row, s_rows - 1);
+            lds_dma16(args.q + (qbase + r) * q_stride + (int64_t)head * D + chunk * 8, lds_addr(qstage + i * 1024));
+        }
+    };
+    // an item's first loads: stages 0 and 1 into ring buffers 0 and 1, and its query rows
+    auto issue_prologue = [&](const Item& x) {
+        const Geo e = geo(x);
+        if (e.n_units > 0) {
+            load_stage_at(e.kbase, e.g, e.sk, 0, 0);
+            if (e.n_stages > 1) load_stage_at(e.kbase, e.g, e.sk, 1, 1);
+            load_q_at(e.qbase, e.head, e.r_lo, e.s_rows);
+        }
+    };
+
+    if (wave == 0) {
+        // reserve an item when the queue holds at least kReserveItems per workgroup
+        const int wg_per_queue = max(1, (int)gridDim.x / nq_queues);
+        const bool ahead = plan.total >= kReserveItems * wg_per_queue;
+        publish(__builtin_amdgcn_readfirstlane(pop()), 0);
+        if (ahead) publish(__builtin_amdgcn_readfirstlane(pop()), 1);
+        else if (lane == 0) mbox[4] = -1;
+        if (lane == 0) mbox[8] = ahead ? 1 : 0;
+    }
     __syncthreads();
+    const bool ahead = __builtin_amdgcn_readfirstlane(mbox[8]) != 0;
+    Item cur = read_rec(0), nxt = read_rec(1);
+    if (cur.a >= 0) issue_prologue(cur);
 
     int it = 0;                                  // items processed
     for (;; ++it) {
-        const int slot = it & 1;
+        if (cur.a < 0) break;
         int k_next = 0;
-        // item fields are uniform: keep them in scalar registers
-        const int it_a = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 0]);
-        if (it_a < 0) break;
-        const int64_t qbase = it_a;
-        const int64_t kbase = MODE == 0 ? qbase : 0;
-        const int s_rows = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 1]);
-        const int sk = MODE == 0 ? s_rows : args.Lk;
-        const int hb = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 2]);
-        const int tg = __builtin_amdgcn_readfirstlane(s_item[4 * slot + 3]);
-        // query position minus key position of (row 0, key 0)
-        const int delta = MODE == 0 ? 0 : args.delta;
-        const bool causal = MODE == 0 ? true : (args.causal != 0);
+        const Geo e = geo(cur);
+        const int64_t qbase = e.qbase;
+        const int64_t kbase = e.kbase;
+        const int s_rows = e.s_rows;
+        const int sk = e.sk;
+        const int head = e.head;
+        const int g = e.g;
+        const int r_lo = e.r_lo;
+        const int n_units = e.n_units;
+        const int n_stages = e.n_stages;
 
-        const int head = hb * hpw + (wave % hpw);
-        const int g = (hb * hpw) / G;
-        const int r_lo = tg * W + (wave / hpw) * kRowsPerWave;   // this wave's first row
-        // keys the workgroup visits
-        const int wg_rmax = min(s_rows, (tg + 1) * W) - 1;
-        int jmax = sk - 1;
-        if (causal) jmax = min(jmax, delta + wg_rmax);
-        const int n_units = (wg_rmax < 0 || jmax < 0) ? 0 : (int)(jmax / kUnit) + 1;
-        const int n_stages = (n_units + 1) / 2;
-
-        // ---- Q^T fragments in registers, loaded through LDS ----
-        // The wave's 64 query rows arrive by direct loads (16 lanes per row, so every load reads
-        // whole 256-byte rows) into a staging tile laid out like a K stage, and the fragments
-        // are then read as the K fragments are: loading the fragments straight from memory,
-        // where each lane reads its own row, takes ≈2K cycles longer per item.  The staging
-        // tiles are ring buffer 2 (waves 0-1), which the first stage turn refills, and the
-        // output tiles (waves 2-3), which the epilogue reuses.  Rows past the sequence's end
-        // repeat its last row (their results are never stored).
         u32x4 qf[kNT][C::kKS];
-        unsigned char* qstage = wave < 2 ? smem[2][wave] : obuf[2 * (wave - 2)];
-        auto load_q = [&]() {
-#pragma unroll
-            for (int i = 0; i < kRowsPerWave / C::kRowsPerBlock; ++i) {
-                const int row = i * C::kRowsPerBlock + lane / C::kChunks;
-                const int chunk = (lane % C::kChunks) ^ swz(row);
-                const int r = min(r_lo + row, s_rows - 1);
-                lds_dma16(args.q + (qbase + r) * q_stride + (int64_t)head * D + chunk * 8, lds_addr(qstage + i * 1024));
-            }
-        };
         // The fragments go to accumulation registers (AGPRs), which the score product reads as
         // its B operand, through one assembly block that also waits for the reads; left to
         // itself the register allocator moves other operands there and adds copies to every
@@ -280,29 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         for (int nt = 0; nt < kNT; ++nt)
             lim0[nt] = causal ? delta + r_lo + nt * 32 + l32 : sk - 1;
 
-        // ---- direct global -> LDS stage loads (K and V of 64 keys) into ring buffer B ----
-        // A whole stage inside the sequence takes a scalar base plus the per-lane offsets; the
-        // last stage clamps its rows to the sequence's last key.
-        auto load_stage = [&](int st, int B) {
-            const int j0 = st * kStage;
-            // uniform base of the stage's first key row (scalar registers) + per-lane offsets
-            const int64_t sofs = (kbase + j0) * kv_stride + (int64_t)g * D;
-            const uint32_t lk = lds_addr(smem[B][0] + wave * C::kBlocksPerWave * 1024);
-            const uint32_t lv = lds_addr(smem[B][1] + wave * C::kBlocksPerWave * 1024);
-            if (j0 + kStage <= sk) {
-                lds_dma16_tiles<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, gofs, lk, lv);
-            } else {
-                uint32_t voff[C::kBlocksPerWave];
-#pragma unroll
-                for (int i = 0; i < C::kBlocksPerWave; ++i) {
-                    const int row = (wave * C::kBlocksPerWave + i) * C::kRowsPerBlock + lane / C::kChunks;
-                    const int chunk = (lane % C::kChunks) ^ swz(row);
-                    const int j = min(j0 + row, sk - 1) - j0;
-                    voff[i] = (uint32_t)((j * kv_stride + chunk * 8) * 2);
-                }
-                lds_dma16_pairs<C::kBlocksPerWave>(args.k + sofs, args.v + sofs, voff, lk, lv);
-            }
-        };
+        auto load_stage = [&](int st, int B) { load_stage_at(kbase, g, sk, st, B); };
 
         // LDS base of a unit's 32 rows: half h of the K (kv = 0) or V (kv = 1) tile of ring
         // buffer buf (uniform)
@@ -460,13 +505,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
             if (i == 2 * NB - 1) dma_tile_end(spread_m0);
         };
+        // this item's first stages and query rows went out at the end of the previous item (or
+        // before the first): wait for them and for the previous item's stores
         auto stage_prologue = [&]() {
-            if (n_units > 0) {
-                load_stage(0, 0);
-                if (n_stages > 1) load_stage(1, 1);
-                load_q();
-                __builtin_amdgcn_s_waitcnt(0x0F70);
-            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);
             __syncthreads();
         };
         // Normalise and write this wave's rows.  The accumulator holds each row split over two
@@ -493,6 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 const int nrows = max(0, min(32, s_rows - row0));
                 float fs = inv;                                    // factor on the accumulator
                 float lout = lse;
+                float a1s = 0.f;                                   // merge: weight on o_acc of row l32
                 if constexpr (MODE == 2) {
                     // Merge into the running result by log-sum-exp: with w = exp(lse - m) over
                     // m = max(lse_acc, lse), o = (w_acc o_acc + w o) / (w_acc + w) and
@@ -516,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                         lout = m + __builtin_amdgcn_logf(w1 + w2) * kLn2;
                     }
                     fs = inv * a2;
-                    if (half == 0) s_a1[wave][l32] = a1;           // read back by the tile lanes
+                    a1s = a1;                                      // (both halves: the row's value)
                 }
                 buf_store_b32(args.lse + (qbase + row0) * (int64_t)H + head, nrows > 0 ? (uint32_t)((nrows - 1) * H * 4 + 4) : 0u,
                               half == 0 ? (uint32_t)(l32 * H * 4) : kDropOffset, lout);
@@ -565,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
 #pragma unroll
                         for (int i = 0; i < kReads; ++i) {
                             const int tr = i * kRowsPerRead + lane / kSlots;
-                            const float a1 = s_a1[wave][tr];
+                            const float a1 = __shfl(a1s, tr);      // from a lane of row tr
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const float t = __uint_as_float(vals[i][e]);
@@ -603,6 +646,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // raised (and the accumulator rescaled) only when a lane's sum of P over a unit exceeds
         // 2^8, which keeps every P <= 2^8, and on a row's first visible unit.
         stage_prologue();
+        // the item after this one, published by wave 0 at the end of the previous item
+        if (ahead && it > 0) nxt = read_rec(0);
         f32x16 o[C::kMT][kNT];
 #pragma unroll
         for (int mt = 0; mt < C::kMT; ++mt)
@@ -769,17 +814,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 value(o, vf, PA);
             }
         }
-        // The next item is taken only now, when this workgroup is about to be free: taking it
-        // earlier would hand out the queue's large items before it is known which workgroup
-        // finishes first.  The atomic's latency passes under the output stores.
-        if (wave == 0) k_next = pop();
-        // Waves 2-3 staged their query rows in the output tiles, and the first workgroup barrier
-        // after read_q is the stage turn of unit 1: an item of a single unit has none, so one
-        // is taken here before any wave overwrites a tile that another may still be reading.
-        if (n_units == 1) __syncthreads();
-        store_rows(o, m, l);
-        if (wave == 0) publish(__builtin_amdgcn_readfirstlane(k_next), slot ^ 1);
-        __syncthreads();
+        if (ahead) {
+            // Every wave is done with the ring and the Q staging: the item after the next is
+            // taken and the next item's first loads go out, both under the output stores.
+            __syncthreads();
+            if (wave == 0 && nxt.a >= 0) k_next = pop();
+            if (nxt.a >= 0) issue_prologue(nxt);
+            store_rows(o, m, l);
+            if (wave == 0 && nxt.a >= 0) publish(__builtin_amdgcn_readfirstlane(k_next), 0);
+            cur = nxt;
+        } else {
+            // The next item is taken only now, when this workgroup is about to be free.  Its
+            // record is in the mailbox after the barrier, and its first loads go out then.
+            if (wave == 0) k_next = pop();
+            store_rows(o, m, l);
+            if (wave == 0) publish(__builtin_amdgcn_readfirstlane(k_next), 0);
+            __syncthreads();
+            cur = read_rec(0);
+            if (cur.a >= 0) issue_prologue(cur);
+        }
     }
 
     if (tid == 0) {
