@@ -42,7 +42,10 @@
 // short items fill the gaps at the end instead of idling CUs.  With 8 head blocks there is one
 // queue per XCD and head block b is served by the XCD b mod 8, so each K/V head's tiles stay in
 // one XCD's L2, until that XCD's queue is empty: its workgroups then help with the other
-// queues.  The order is decoded on the device from cu_seqlens, without a planning launch.
+// queues.  The order is decoded on the device from cu_seqlens, without a planning launch.  When
+// a launch has at least 8 items per workgroup, a workgroup holds one item in reserve, so that the
+// next item's first loads go out under the current item's output stores; with fewer, each item
+// is taken when its workgroup is about to be free (taking items early would unbalance the CUs).
 #include "device_common.h"
 
 namespace hdp {
