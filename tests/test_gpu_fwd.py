@@ -165,6 +165,26 @@ def test_more_than_64_sequences_full():
     assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
 
 
+def test_many_items_per_workgroup_full():
+    # 300 short sequences at 32 query heads (8 head blocks, one queue per XCD): each queue holds
+    # sum ceil(len / 64) ~ 450 items, at least 8 per workgroup on 256 CUs, so every workgroup
+    # holds one item in reserve and issues the next item's first loads under its output stores.
+    # Every row of every head against the oracle.
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 129, size=300)]
+    lengths[7], lengths[150] = 0, 1
+    w, q, k, v, cu = varlen_case(lengths, 32, 8, 128, seed=31)
+    items_per_queue = sum((n + 63) // 64 for n in lengths)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    reserve = items_per_queue >= 8 * max(1, cus // 8)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
+    out, lse = run_fwd(q, k, v, cu, w.scale)
+    e_out, e_lse = max_abs(out, ro), max_abs(lse, rl)
+    print("%d sequences, %d tokens, %d items per queue (reserve %s): max|dout|=%.3g max|dlse|=%.3g"
+          % (len(lengths), int(cu[-1]), items_per_queue, reserve, e_out, e_lse))
+    assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
+
+
 @pytest.mark.parametrize("lengths", [[4096, 17, 0, 300], [4097, 5, 64]])
 def test_work_queue_level_boundary_sampled(lengths):
     # with 4 query heads per key/value head an item spans 64 rows: a 4096-token sequence has 64
