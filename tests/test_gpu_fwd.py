@@ -49,10 +49,12 @@ def test_tiny_fp32_pack_full():
 
 
 @pytest.mark.parametrize("lengths,H,Hkv,D", [([1, 5, 37, 0, 260, 33], 8, 2, 128),
-                                             ([3, 100, 64, 131], 6, 3, 64)])
+                                             ([3, 100, 64, 131], 6, 3, 64),
+                                             ([300, 7, 0, 257, 129], 4, 4, 64)])
 def test_fp32_ragged_pack_full(lengths, H, Hkv, D):
-    # grouped heads, empty and single-token sequences, rows past the 32 that one pass of the
-    # kernel's waves covers, and key counts that are not multiples of its 4-key blocks
+    # grouped heads, empty and single-token sequences, rows past one row block, key counts that
+    # are not multiples of the kernel's 4-key blocks, and sequences whose keys span more than one
+    # LDS chunk (128 keys at D = 128, 256 at D = 64)
     w, q, k, v, cu = varlen_case(lengths, H, Hkv, D, 23, dtype="f32")
     ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale)
     qg, kg, vg = to_gpu(q, k, v)
