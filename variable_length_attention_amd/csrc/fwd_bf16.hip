@@ -32,9 +32,10 @@
 // Softmax uses exp2 with scale*log2(e) folded into one FMA and a lazy reference instead of an
 // exact running max (exact arithmetic is unchanged because numerator and denominator share the
 // reference).  The common path computes no max at all: P = exp2(S c2 - m) is summed in fp32
-// and goes straight to bf16.  Only when a lane's sum over a unit exceeds 2^8 (so possibly
-// some P > 2^8), or on a row's first visible unit, does a branch take the row max, raise the
-// reference and rescale the accumulator.
+// and goes straight to bf16.  The reference starts at the row max of an item's first unit,
+// taken before its exponentials.  Only when a lane's sum over a unit exceeds 2^8 (so possibly
+// some P > 2^8), or on the first visible unit of a row whose first unit is wholly masked, does a
+// branch take the row max, raise the reference and rescale the accumulator.
 //
 // Scheduling.  The kernel is persistent (one workgroup per CU).  Items are popped from a queue
 // in order of decreasing cost, where the cost of a query tile is the number of key tiles it
@@ -645,9 +646,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // Step u issues the value product of unit u-1 and the score product of unit u+1 and
         // runs the softmax of unit u; the three are independent.  The running max m is a
         // reference, not necessarily the max: numerator and denominator share it, so the result
-        // is exact whatever reference is used as long as no P overflows or all underflow.  It is
-        // raised (and the accumulator rescaled) only when a lane's sum of P over a unit exceeds
-        // 2^8, which keeps every P <= 2^8, and on a row's first visible unit.
+        // is exact whatever reference is used as long as no P overflows or all underflow.  It
+        // starts at the first unit's row max and is raised (and the accumulator rescaled) only
+        // when a lane's sum of P over a unit exceeds 2^8, which keeps every P <= 2^8, and on the
+        // first visible unit of a row that saw no key before.
         stage_prologue();
         // the item after this one, published by wave 0 at the end of the previous item
         if (ahead && it > 0) nxt = read_rec(0);
@@ -804,6 +806,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
             }
             read_v(0, 0, vf);   // multiplied by the zero P of unit -1
             if (!unit_full(0)) apply_mask(0, SA);
+            // the reference starts at the first unit's row max, so the first step takes no
+            // rescale branch (a row whose first unit is wholly masked keeps -inf and takes it)
+            {
+                float tmax[kNT];
+                row_max(SA, tmax);
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    const bool none = tmax[nt] == -INFINITY;
+                    m[nt] = tmax[nt];
+                    mref[nt] = none ? 0.f : tmax[nt];
+                    thr[nt] = none ? -1.f : kLazySum;
+                }
+            }
             int u = 0;
             for (; u + 1 < n_units; u += 2) {
                 step(u, false, SA, SB, PA, PB);
