@@ -299,11 +299,16 @@ def detail_rows(torch, ops, synth):
 def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
     """Per-workgroup busy time of the forward on the 8K slice and both 32K micro-batches: the
     persistent kernel runs one workgroup per CU, each records when it started and when it finished
-    its last item (hdp_set_trace).  Reported per workload, averaged over `launches` launches:
-    finish time of the last / mean / first workgroup after the first one started, in us, and the
-    last workgroup of each XCD (workgroup w runs on XCD w mod 8)."""
+    its last item (hdp_set_trace), and for each item when it started, when its first loads had
+    landed and when its last step was done (hdp_set_item_trace).  Reported per workload, averaged
+    over `launches` launches: finish time of the last / mean / first workgroup after the first one
+    started, in us, the last workgroup of each XCD (workgroup w runs on XCD w mod 8), and each
+    workgroup's time split into waiting for first loads, steps (fitted as a cost per 32-key unit
+    plus a fixed cost per item) and item transitions (output stores, pop, next item's loads)."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     trace = torch.zeros(4 * n_cu, dtype=torch.int64, device="cuda")
+    slots = 32
+    item_buf = torch.zeros(4 * slots * n_cu, dtype=torch.int64, device="cuda")
     out = {}
     for make in (synth.packed_slice_8k, synth.microbatch_32k_long, synth.microbatch_32k_short):
         w = make()
@@ -316,17 +321,32 @@ def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
             ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale, out=o, lse=lse)
 
         settle_clock(step, torch, 300.0)
-        rows = []
+        rows, recs = [], []
         ops.hdp_set_trace(trace)
+        ops.hdp_set_item_trace(item_buf, slots)
         try:
             for _ in range(launches):
                 trace.zero_()
+                item_buf.zero_()
                 step()
                 torch.cuda.synchronize()
                 t = trace.view(n_cu, 4).cpu().numpy()
                 rows.append(t.copy())
+                recs.append(item_buf.view(n_cu, slots, 4).cpu().numpy())
         finally:
             ops.hdp_set_trace(None)
+            ops.hdp_set_item_trace(None)
+        # (records are read after the launches: host work between launches would let the clock drop)
+        items_rows = []
+        for t, it in zip(rows, recs):
+            for b in range(n_cu):
+                n = int(t[b, 2])
+                for i in range(min(n, slots)):
+                    if i + 1 < n and i + 1 >= slots:
+                        continue                           # next start not recorded
+                    nxt = it[b, i + 1, 0] if i + 1 < n else t[b, 1]
+                    a0, a1, a2, nu = (int(x) for x in it[b, i])
+                    items_rows.append((nu, (a1 - a0) / 100.0, (a2 - a1) / 100.0, (nxt - a2) / 100.0))
         fin, busy, items, xcd_last = [], [], [], []
         for t in rows:
             t0 = int(t[:, 0].min())
@@ -346,6 +366,19 @@ def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
             "busy_over_last_finish": round(float(busy.mean(axis=1).mean() / fin.max(axis=1).mean()), 4),
             "items_per_workgroup_min_mean_max": [int(items.min()), round(float(items.mean()), 2), int(items.max())],
             "xcd_last_finish_us": [round(float(x), 2) for x in np.array(xcd_last).mean(axis=0)],
+        }
+        r = np.array(items_rows, dtype=np.float64)
+        nu, wait, steps, trans = r[:, 0], r[:, 1], r[:, 2], r[:, 3]
+        per_unit, fixed = np.linalg.lstsq(np.vstack([nu, np.ones_like(nu)]).T, steps, rcond=None)[0]
+        per_wg = 1.0 / (launches * n_cu)
+        out[w.name]["items"] = {
+            "records": int(len(r)),
+            "per_workgroup_us_wait_steps_transitions": [round(float(wait.sum() * per_wg), 2), round(float(steps.sum() * per_wg), 2),
+                                                        round(float(trans.sum() * per_wg), 2)],
+            "per_item_us_wait_transition": [round(float(wait.mean()), 3), round(float(trans.mean()), 3)],
+            "transition_us_p10_p90": [round(float(np.percentile(trans, 10)), 3), round(float(np.percentile(trans, 90)), 3)],
+            "steps_us_per_unit_and_fixed_per_item": [round(float(per_unit), 4), round(float(fixed), 3)],
+            "mean_units_per_item": round(float(nu.mean()), 2),
         }
         del qq, kk, vv, o, lse
     return out

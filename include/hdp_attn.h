@@ -269,6 +269,20 @@ int hdp_probe_clock(int32_t iters, double* mhz, hipStream_t stream);
  */
 int hdp_set_trace(long long* trace, int32_t capacity);
 
+/*
+ * Measurement helper, not part of the attention path: per-item timeline of the same forward
+ * launches.  With items != NULL (device memory of 4 x slots x capacity int64, slots > 0) every
+ * later forward launch whose persistent grid fits the capacity writes, for the i-th item
+ * (i < slots) that workgroup w processes, at items[4 (w slots + i) + 0..3]: the real-time counter
+ * (100 MHz) when the item started, when its first key/value stages and query rows had landed in
+ * LDS, when its last step was done (the output stores and the next item's pop follow), and the
+ * number of 32-key units it ran.  Records past the items a workgroup processed are left as they
+ * were.  capacity 0 turns it off; HDP_ERR_INVALID_ARG for a negative capacity or slots, or for
+ * capacity > 0 with a NULL buffer or slots = 0.  With hdp_set_trace this splits each workgroup's
+ * time into waiting for first loads, steps and item transitions.
+ */
+int hdp_set_item_trace(long long* items, int32_t capacity, int32_t slots);
+
 /* Static text for a status code. */
 const char* hdp_status_string(int status);
 

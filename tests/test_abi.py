@@ -162,6 +162,19 @@ def test_other_entry_points_validate_before_touching_the_gpu():
         assert _lib.lib().hdp_status_string(st).startswith(b"HDP_")
 
 
+def test_trace_helpers_validate_their_arguments():
+    # measurement helpers only store a device pointer: no HIP call, so they run here
+    L = _lib.lib()
+    assert L.hdp_set_trace(NULL, -1) == _lib.HDP_ERR_INVALID_ARG
+    assert L.hdp_set_trace(NULL, 4) == _lib.HDP_ERR_INVALID_ARG
+    assert L.hdp_set_item_trace(NULL, -1, 4) == _lib.HDP_ERR_INVALID_ARG
+    assert L.hdp_set_item_trace(FAKE, 4, -1) == _lib.HDP_ERR_INVALID_ARG
+    assert L.hdp_set_item_trace(NULL, 4, 4) == _lib.HDP_ERR_INVALID_ARG
+    assert L.hdp_set_item_trace(FAKE, 4, 0) == _lib.HDP_ERR_INVALID_ARG
+    assert L.hdp_set_item_trace(NULL, 0, 0) == _lib.HDP_OK
+    assert L.hdp_set_trace(NULL, 0) == _lib.HDP_OK
+
+
 def test_clock_probe_validates_before_any_hip_call():
     lib = _lib.lib()
     import ctypes

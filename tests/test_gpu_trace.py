@@ -1,0 +1,83 @@
+"""GPU: the forward's workgroup and per-item timelines (measurement helpers hdp_set_trace and
+hdp_set_item_trace) account for every work item exactly once.
+
+The work items of the packed forward are the query-row tiles of every sequence times the head
+blocks, each visiting the 32-key units up to its last row (causal); their cost grows with the
+square of the sequence length (research digest "ByteScale: Communication-Efficient Scaling of LLM
+Training with a 2048K Context Length on 16384 GPUs", §2, "Imbalanced computation"), which is
+what the longest-first queue balances.  Whatever workgroup takes an item, the items recorded
+over all workgroups must be exactly the items of the batch: their number and their units add up
+to the host-side count, each record's timestamps are ordered, and the result is still correct.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL_BF16_LSE, TOL_BF16_OUT, lse_close, max_abs
+from variable_length_attention_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+ROWS = 64           # query rows per item (256 row-heads over 4 query heads per item)
+UNIT = 32           # keys per unit
+
+
+def expected_items(lengths, H, heads_per_item=4):
+    """Host count of the forward's items and their units (causal: up to the item's last row)."""
+    units = []
+    for L in lengths:
+        for t in range(math.ceil(L / ROWS)):
+            last_row = min(L, (t + 1) * ROWS) - 1
+            units += [last_row // UNIT + 1] * (H // heads_per_item)
+    return len(units), sum(units)
+
+
+@pytest.mark.parametrize("lengths", [None, [1, 2, 63, 64, 65, 700, 5, 1500, 31, 128, 129]])
+def test_item_trace_accounts_for_every_item_once(lengths):
+    if lengths is None:
+        w = synth.packed_slice_8k()
+    else:
+        w = synth.Workload("case", "varlen", 32, 8, 128, "bf16", list(lengths), 161)
+    q, k, v = synth.varlen_tensors(w)
+    cu = synth.cu_seqlens(w.lengths)
+    qg, kg, vg, cug = q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(cu).cuda()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    slots = 64
+    trace = torch.zeros(4 * n_cu, dtype=torch.int64, device="cuda")
+    items = torch.zeros(4 * slots * n_cu, dtype=torch.int64, device="cuda")
+    ops.hdp_set_trace(trace)
+    ops.hdp_set_item_trace(items, slots)
+    try:
+        out, lse = ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale)
+        torch.cuda.synchronize()
+    finally:
+        ops.hdp_set_trace(None)
+        ops.hdp_set_item_trace(None)
+    t = trace.view(n_cu, 4).cpu().numpy()
+    it = items.view(n_cu, slots, 4).cpu().numpy()
+    n_items, n_units = expected_items(w.lengths, w.H)
+    done = t[:, 2]
+    assert done.max() <= slots
+    assert int(done.sum()) == n_items
+    got_units = 0
+    for b in range(n_cu):
+        n = int(done[b])
+        assert t[b, 0] <= t[b, 1]
+        for i in range(n):
+            a0, a1, a2, nu = (int(x) for x in it[b, i])
+            nxt = int(it[b, i + 1, 0]) if i + 1 < n else int(t[b, 1])
+            assert t[b, 0] <= a0 <= a1 <= a2 <= nxt, (b, i)
+            assert nu >= 1
+            got_units += nu
+        assert not it[b, n:].any()                 # nothing recorded past the items it ran
+    assert got_units == n_units
+    print("items %d units %d over %d workgroups (max %d per workgroup)" % (n_items, n_units, n_cu, done.max()))
+    # the traced launch computed the right result (every 97th row checked on the slice)
+    rows = np.arange(0, q.shape[0], 97 if lengths is None else 1)
+    ro, rl = oracle.varlen_fwd(q, k, v, cu, w.scale, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    assert max_abs(out[idx], ro) <= TOL_BF16_OUT
+    lse_close(lse[idx], rl, TOL_BF16_LSE)

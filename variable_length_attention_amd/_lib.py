@@ -39,6 +39,7 @@ SIGNATURES = {
     "hdp_plan_balance": (I32, [P, P, I32, I32, U64, P, P]),
     "hdp_probe_clock": (I32, [I32, P, P]),
     "hdp_set_trace": (I32, [P, I32]),
+    "hdp_set_item_trace": (I32, [P, I32, I32]),
     "hdp_status_string": (ctypes.c_char_p, [I32]),
     "hdp_release_workspace": (I32, []),
 }

@@ -117,6 +117,10 @@ int heads_per_item(int32_t H, int32_t Hkv) {
 // Forward workgroup trace (measurement helper): a device buffer and its capacity in workgroups.
 std::atomic<long long*> g_trace{nullptr};
 std::atomic<int> g_trace_cap{0};
+// Per-item forward timeline (measurement helper): buffer, capacity in workgroups, items each.
+std::atomic<long long*> g_itrace{nullptr};
+std::atomic<int> g_itrace_cap{0};
+std::atomic<int> g_itrace_slots{0};
 
 void schedule(int cus, const StreamState* st, int32_t H, int32_t Hkv, hdp::FwdArgs& a, int& grid) {
     a.hpw = heads_per_item(H, Hkv);
@@ -125,6 +129,9 @@ void schedule(int cus, const StreamState* st, int32_t H, int32_t Hkv, hdp::FwdAr
     a.nqueues = (nhb % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0) ? hdp::kMaxQueues : 1;
     a.counters = st->counters;
     a.trace = g_trace_cap.load() >= grid ? g_trace.load() : nullptr;
+    a.item_trace = g_itrace_cap.load() >= grid ? g_itrace.load() : nullptr;
+    a.item_slots = a.item_trace != nullptr ? g_itrace_slots.load() : 0;
+    if (a.item_slots <= 0) a.item_trace = nullptr;
 }
 
 // sum_{r=0}^{n-1} clamp(a + r, 0, cap), exactly.
@@ -451,6 +458,15 @@ int hdp_set_trace(long long* trace, int32_t capacity) {
     g_trace_cap.store(0);
     g_trace.store(capacity > 0 ? trace : nullptr);
     g_trace_cap.store(capacity);
+    return HDP_OK;
+}
+
+int hdp_set_item_trace(long long* items, int32_t capacity, int32_t slots) {
+    if (capacity < 0 || slots < 0 || (capacity > 0 && (items == nullptr || slots == 0))) return HDP_ERR_INVALID_ARG;
+    g_itrace_cap.store(0);
+    g_itrace.store(capacity > 0 ? items : nullptr);
+    g_itrace_slots.store(capacity > 0 ? slots : 0);
+    g_itrace_cap.store(capacity);
     return HDP_OK;
 }
 

@@ -292,6 +292,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     for (;; ++it) {
         if (cur.a < 0) break;
         int k_next = 0;
+        // per-item timeline (measurement only): one record per item of the first item_slots
+        long long* const itr = (args.item_trace != nullptr && tid == 0 && it < args.item_slots)
+            ? args.item_trace + ((int64_t)blockIdx.x * args.item_slots + it) * kItemTraceWords : nullptr;
+        if (itr != nullptr) itr[0] = (long long)__builtin_amdgcn_s_memrealtime();
         const Geo e = geo(cur);
         const int64_t qbase = e.qbase;
         const int64_t kbase = e.kbase;
@@ -651,6 +655,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         // when a lane's sum of P over a unit exceeds 2^8, which keeps every P <= 2^8, and on the
         // first visible unit of a row that saw no key before.
         stage_prologue();
+        if (itr != nullptr) {
+            itr[1] = (long long)__builtin_amdgcn_s_memrealtime();
+            itr[3] = n_units;
+        }
         // the item after this one, published by wave 0 at the end of the previous item
         if (ahead && it > 0) nxt = read_rec(0);
         f32x16 o[C::kMT][kNT];
@@ -832,6 +840,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
                 value(o, vf, PA);
             }
         }
+        if (itr != nullptr) itr[2] = (long long)__builtin_amdgcn_s_memrealtime();
         if (ahead) {
             // Every wave is done with the ring and the Q staging: the item after the next is
             // taken and the next item's first loads go out, both under the output stores.

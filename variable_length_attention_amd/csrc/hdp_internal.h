@@ -39,9 +39,15 @@ struct FwdArgs {
     // measurement: null, or kTraceWords words per workgroup (real-time counter at start and
     // end, items processed, unused)
     long long* trace;
+    // measurement: null, or item_slots records of kItemTraceWords words per workgroup, one per
+    // item of its first item_slots (real-time counter at the item's start, when its first loads
+    // had landed and when its last step was done; its 32-key units)
+    long long* item_trace;
+    int32_t item_slots;
 };
 
 constexpr int kTraceWords = 4;
+constexpr int kItemTraceWords = 4;
 
 struct F32Args {
     const float* q;

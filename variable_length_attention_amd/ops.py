@@ -325,5 +325,18 @@ def hdp_set_trace(trace: Optional[torch.Tensor]) -> None:
     _lib.check("hdp_set_trace", _lib.lib().hdp_set_trace(trace.data_ptr(), trace.numel() // 4))
 
 
+def hdp_set_item_trace(items: Optional[torch.Tensor], slots: int = 0) -> None:
+    """Per-item forward timeline into an int64 device tensor of 4 x slots words per workgroup
+    (None: off).  Measurement helper."""
+    if items is None:
+        _lib.check("hdp_set_item_trace", _lib.lib().hdp_set_item_trace(None, 0, 0))
+        return
+    _dev_tensor("items", items, torch.int64, 1)
+    if slots <= 0:
+        raise ValueError("slots must be positive")
+    _lib.check("hdp_set_item_trace",
+               _lib.lib().hdp_set_item_trace(items.data_ptr(), items.numel() // (4 * slots), int(slots)))
+
+
 def hdp_release_workspace() -> None:
     _lib.check("hdp_release_workspace", _lib.lib().hdp_release_workspace())
