@@ -304,7 +304,8 @@ def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
     over `launches` launches: finish time of the last / mean / first workgroup after the first one
     started, in us, the last workgroup of each XCD (workgroup w runs on XCD w mod 8), and each
     workgroup's time split into waiting for first loads, steps (fitted as a cost per 32-key unit
-    plus a fixed cost per item) and item transitions (output stores, pop, next item's loads)."""
+    plus a fixed cost per item) and item transitions (output stores, pop, next item's loads).
+    Backward (8K slice, one 8K sequence): when each workgroup left the dK/dV queue and finished."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     trace = torch.zeros(4 * n_cu, dtype=torch.int64, device="cuda")
     slots = 32
@@ -381,6 +382,44 @@ def cu_timeline(torch, ops, synth, launches: int = 20) -> dict:
             "mean_units_per_item": round(float(nu.mean()), 2),
         }
         del qq, kk, vv, o, lse
+    # backward: each workgroup records its start, when it left the dK/dV queue and its end
+    for make in (synth.fwd_bwd_8k_slice, synth.fwd_bwd_8k_single):
+        w = make()
+        qq, kk, vv, dd = (t.cuda() for t in synth.varlen_tensors(w, with_dout=True))
+        cu = torch.from_numpy(synth.cu_seqlens(w.lengths)).cuda()
+        o, lse = ops.hdp_attn_varlen_fwd(qq, kk, vv, cu, w.scale)
+        dq, dk, dv = torch.empty_like(qq), torch.empty_like(kk), torch.empty_like(vv)
+
+        def bstep():
+            ops.hdp_attn_varlen_bwd(qq, kk, vv, o, lse, dd, cu, w.scale, dq=dq, dk=dk, dv=dv)
+
+        settle_clock(bstep, torch, 300.0)
+        rows = []
+        ops.hdp_set_trace(trace)
+        try:
+            for _ in range(launches):
+                trace.zero_()
+                bstep()
+                torch.cuda.synchronize()
+                rows.append(trace.view(n_cu, 4).cpu().numpy().copy())
+        finally:
+            ops.hdp_set_trace(None)
+        import numpy as np
+        left, fin, busy = [], [], []
+        for t in rows:
+            t0 = int(t[:, 0].min())
+            left.append((t[:, 1] - t0) / 100.0)
+            fin.append((t[:, 2] - t0) / 100.0)
+            busy.append((t[:, 2] - t[:, 0]) / 100.0)
+        left, fin, busy = np.array(left), np.array(fin), np.array(busy)
+        mm = lambda a: [round(float(a.min(axis=1).mean()), 1), round(float(a.mean()), 1), round(float(a.max(axis=1).mean()), 1)]
+        out["bwd." + w.name] = {
+            "n_seq": len(w.lengths), "launches": launches, "workgroups": n_cu,
+            "left_dkdv_queue_us_min_mean_max": mm(left),
+            "finish_us_min_mean_max": mm(fin),
+            "busy_over_last_finish": round(float(busy.mean(axis=1).mean() / fin.max(axis=1).mean()), 4),
+        }
+        del qq, kk, vv, dd, o, lse, dq, dk, dv
     return out
 
 

@@ -265,6 +265,9 @@ int hdp_probe_clock(int32_t iters, double* mhz, hipStream_t stream);
  * fits the capacity writes, for workgroup w: trace[4w] = the real-time counter (100 MHz) when
  * it started, trace[4w+1] = when it finished its last item, trace[4w+2] = items it processed,
  * trace[4w+3] = 0.  The buffer is overwritten by each such launch.  capacity 0 turns it off.
+ * Backward launches (hdp_attn_varlen_bwd, hdp_attn_chunk_bwd) write, for workgroup w:
+ * trace[4w] = when it started, trace[4w+1] = when it left the dK/dV work queue (it then takes
+ * dQ items), trace[4w+2] = when it finished, trace[4w+3] = 0.
  * This is how the FLOP-ordered scheduling's balance across CUs is measured.
  */
 int hdp_set_trace(long long* trace, int32_t capacity);

@@ -81,3 +81,26 @@ def test_item_trace_accounts_for_every_item_once(lengths):
     idx = torch.from_numpy(rows).cuda()
     assert max_abs(out[idx], ro) <= TOL_BF16_OUT
     lse_close(lse[idx], rl, TOL_BF16_LSE)
+
+
+def test_backward_trace_is_ordered_and_changes_nothing():
+    # the backward is deterministic: a traced call gives bit-identical gradients
+    w = synth.Workload("case", "varlen", 32, 8, 128, "bf16", [700, 1, 65, 1300, 31], 162)
+    q, k, v, do = synth.varlen_tensors(w, with_dout=True)
+    cu = synth.cu_seqlens(w.lengths)
+    qg, kg, vg, dg, cug = q.cuda(), k.cuda(), v.cuda(), do.cuda(), torch.from_numpy(cu).cuda()
+    o, lse = ops.hdp_attn_varlen_fwd(qg, kg, vg, cug, w.scale)
+    ref = ops.hdp_attn_varlen_bwd(qg, kg, vg, o, lse, dg, cug, w.scale)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    trace = torch.zeros(4 * n_cu, dtype=torch.int64, device="cuda")
+    ops.hdp_set_trace(trace)
+    try:
+        got = ops.hdp_attn_varlen_bwd(qg, kg, vg, o, lse, dg, cug, w.scale)
+        torch.cuda.synchronize()
+    finally:
+        ops.hdp_set_trace(None)
+    t = trace.view(n_cu, 4).cpu().numpy()
+    assert (t[:, 0] > 0).all()
+    assert (t[:, 0] <= t[:, 1]).all() and (t[:, 1] <= t[:, 2]).all() and (t[:, 3] == 0).all()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -207,6 +207,7 @@ int launch_varlen_bwd(const void* q, const void* k, const void* v, const void* o
     const bool kv8 = Hkv % kMaxQueues == 0 && grid % kMaxQueues == 0;
     a.nqueues_q = q8 ? kMaxQueues : 1;
     a.nqueues_kv = kv8 ? kMaxQueues : 1;
+    a.trace = g_trace_cap.load() >= grid ? g_trace.load() : nullptr;
     return launch_bwd(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 
@@ -450,6 +451,7 @@ int hdp_attn_chunk_bwd(const void* q_slice, int32_t Lq, const void* k_chunk, con
     const bool kv8 = Hkv % hdp::kMaxQueues == 0 && grid % hdp::kMaxQueues == 0;
     a.nqueues_q = q8 ? hdp::kMaxQueues : 1;
     a.nqueues_kv = kv8 ? hdp::kMaxQueues : 1;
+    a.trace = g_trace_cap.load() >= grid ? g_trace.load() : nullptr;
     return hdp::launch_bwd_chunk(a, D, grid, stream) == hipSuccess ? HDP_OK : HDP_ERR_HIP;
 }
 

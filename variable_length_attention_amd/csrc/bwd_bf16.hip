@@ -970,9 +970,17 @@ template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwd_kernel(BwdArgs args) {
     constexpr int kLds = dkdv_lds_bytes<D>() > dq_lds_bytes<D>() ? dkdv_lds_bytes<D>() : dq_lds_bytes<D>();
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
+    // workgroup timeline (measurement only): start, leaving the dK/dV queue, end
+    long long* const tr = (args.trace != nullptr && threadIdx.x == 0) ? args.trace + (int64_t)blockIdx.x * kTraceWords : nullptr;
+    if (tr != nullptr) tr[0] = (long long)__builtin_amdgcn_s_memrealtime();
     dkdv_body<D, MODE>(args, lds, args.counters);
+    if (tr != nullptr) tr[1] = (long long)__builtin_amdgcn_s_memrealtime();
     __syncthreads();
     dq_body<D, MODE>(args, lds, args.counters + kCounterSetInts);
+    if (tr != nullptr) {
+        tr[2] = (long long)__builtin_amdgcn_s_memrealtime();
+        tr[3] = 0;
+    }
     if (threadIdx.x == 0) queue_finish(args.counters);
 }
 

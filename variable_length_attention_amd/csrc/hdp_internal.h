@@ -101,6 +101,9 @@ struct BwdArgs {
     int32_t hpw;            // query heads per dQ item
     int32_t nqueues_q;      // queues of the dQ kernel (8 or 1)
     int32_t nqueues_kv;     // queues of the dK/dV kernel (8 or 1)
+    // measurement: null, or kTraceWords words per workgroup (real-time counter at its start,
+    // when it left the dK/dV queue and at its end; unused)
+    long long* trace;
 };
 
 // Launchers (return hipSuccess or the launch error).  `grid` is the persistent grid size.
