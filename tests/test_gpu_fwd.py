@@ -167,7 +167,8 @@ def test_more_than_64_sequences_full():
     assert e_out <= TOL_BF16_OUT and e_lse <= TOL_BF16_LSE
 
 
-def test_many_items_per_workgroup_full():
+@pytest.mark.parametrize("D", [128, 64])
+def test_many_items_per_workgroup_full(D):
     # 300 short sequences at 32 query heads (8 head blocks, one queue per XCD): each queue holds
     # sum ceil(len / 64) ~ 450 items, at least 8 per workgroup on 256 CUs, so every workgroup
     # holds one item in reserve and issues the next item's first loads under its output stores.
@@ -175,7 +176,7 @@ def test_many_items_per_workgroup_full():
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.integers(1, 129, size=300)]
     lengths[7], lengths[150] = 0, 1
-    w, q, k, v, cu = varlen_case(lengths, 32, 8, 128, seed=31)
+    w, q, k, v, cu = varlen_case(lengths, 32, 8, D, seed=31)
     items_per_queue = sum((n + 63) // 64 for n in lengths)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     reserve = items_per_queue >= 8 * max(1, cus // 8)
@@ -366,6 +367,47 @@ def test_chunk_merge_equals_partials_merged_by_the_oracle(Lq, q_off, pieces, cau
     lse_close(l_acc, rl, TOL_BF16_LSE)
     assert max_abs(ob, ro) <= TOL_BF16_OUT
     assert torch.equal(ob.view(torch.int16), o_acc.to(torch.bfloat16).view(torch.int16))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_chunk_modes_with_an_item_in_reserve_sampled(D):
+    # A 20,000-row slice gives 313 row tiles per head block (one queue per XCD): at least 8 items
+    # per workgroup, so the chunk and fused-merge kernels hold one item in reserve and issue the
+    # next item's first loads under the current item's output (and merge) traffic.  One chunk
+    # fully in the past, one crossing the slice's first rows (digest ring model, §3.2).
+    H, Hkv, Lq, q_off = 32, 8, 20000, 20000
+    pieces = [(0, 300), (19900, 400)]
+    rng = np.random.default_rng(181 + D)
+    S = max(o + l for o, l in pieces)
+    q = synth.normal(rng, (Lq, H, D), "bf16")
+    k = synth.normal(rng, (S, Hkv, D), "bf16")
+    v = synth.normal(rng, (S, Hkv, D), "bf16")
+    scale = 1 / math.sqrt(D)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert (Lq + 63) // 64 >= 8 * max(1, cus // 8)               # reserve mode in both kernels
+    qg, kg, vg = to_gpu(q, k, v)
+    rows = boundary_rows(Lq, 37, extra=(1, 2, 99, 100, 101))
+    idx = torch.from_numpy(rows).cuda()
+    # chunk partial (no merge) of the crossing chunk
+    ko, kl = pieces[1]
+    o, lse = ops.hdp_attn_chunk_partial(qg, kg[ko:ko + kl], vg[ko:ko + kl], q_off, ko, True, scale)
+    # fused ring steps over both chunks
+    o_acc = torch.full((Lq, H, D), float("nan"), device="cuda")
+    l_acc = torch.full((Lq, H), -float("inf"), device="cuda")
+    ob = torch.empty((Lq, H, D), dtype=torch.bfloat16, device="cuda")
+    for i, (po, pl) in enumerate(pieces):
+        ops.hdp_attn_chunk_merge(qg, kg[po:po + pl], vg[po:po + pl], q_off, po, o_acc, l_acc, True, scale,
+                                 out_bf16=ob if i == len(pieces) - 1 else None)
+    torch.cuda.synchronize()
+    co, cl = oracle.chunk_partial(q, k[ko:ko + kl], v[ko:ko + kl], q_off, ko, True, scale, rows=rows)
+    e_o, e_l = max_abs(o[idx], co), lse_close(lse[idx], cl, TOL_BF16_LSE)
+    ro, rl = ring_reference(q, k, v, q_off, pieces, True, scale, rows=rows)
+    e_m = max_abs(o_acc[idx], ro)
+    e_ml = lse_close(l_acc[idx], rl, TOL_BF16_LSE)
+    print("D=%d, %d sampled rows: partial max|do|=%.3g max|dlse|=%.3g; merged max|do|=%.3g max|dlse|=%.3g"
+          % (D, len(rows), e_o, e_l, e_m, e_ml))
+    assert e_o <= TOL_BF16_OUT and e_m <= TOL_BF16_OUT
+    assert max_abs(ob[idx], ro) <= TOL_BF16_OUT
 
 
 def test_chunk_merge_agrees_with_partial_then_merge():
