@@ -161,7 +161,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
     // is taken when the workgroup is about to be free and its loads go out at its start.
     // Every queue holds the same items (for its own head blocks).  A workgroup whose queue is
     // empty takes the remaining items of the other XCDs' queues in turn: the XCDs do not all
-    // run at the same speed, and otherwise the launch waits for the slowest one's queue.
+    // run at the same speed, and otherwise the launch waits for the slowest one's queue.  It
+    // first reads all the queues it has not tried at once, so that at the end of a launch, when
+    // they are all dry, it stops after one round trip instead of one per queue.
     int src_q = queue;
     int stolen = 0;
     // the atomic's result is in lane 0; callers take it with readfirstlane, so the decode that
@@ -172,6 +174,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdArgs args) {
         return k;
     };
     auto publish = [&](int k, int slot) {
+        if (k >= plan.total && stolen < nq_queues - 1) {
+            // this queue is dry: read every queue not yet tried at once (lane j: the j-th next
+            // queue, an atomic add of 0 that takes nothing, waited in the same block) and skip
+            // those already dry (a counter only grows)
+            const int left = nq_queues - 1 - stolen;
+            int seen = plan.total;
+            if (lane < left) {
+                const int* cq = &args.counters[((queue + stolen + 1 + lane) % nq_queues) * kQueueStride];
+                asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)"
+                             : "=v"(seen) : "v"(cq), "v"(0) : "memory");
+            }
+            const unsigned long long open = __ballot(lane < left && seen < plan.total);
+            stolen = open == 0 ? nq_queues - 1 : stolen + (int)__builtin_ctzll(open);
+        }
         while (k >= plan.total && stolen < nq_queues - 1) {
             ++stolen;
             src_q = (queue + stolen) % nq_queues;
