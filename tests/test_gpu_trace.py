@@ -104,3 +104,45 @@ def test_backward_trace_is_ordered_and_changes_nothing():
     assert (t[:, 0] <= t[:, 1]).all() and (t[:, 1] <= t[:, 2]).all() and (t[:, 3] == 0).all()
     for a, b in zip(ref, got):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_item_trace_of_a_ring_chunk_counts_every_row_tile_once():
+    # chunk mode: the items are the slice's 64-row tiles times the head blocks, whatever the chunk
+    H, Hkv, D, Lq, Lk = 32, 8, 128, 1000, 300
+    rng = np.random.default_rng(163)
+    q = synth.normal(rng, (Lq, H, D), "bf16")
+    k = synth.normal(rng, (Lk, Hkv, D), "bf16")
+    v = synth.normal(rng, (Lk, Hkv, D), "bf16")
+    scale = 1 / math.sqrt(D)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    slots = 16
+    trace = torch.zeros(4 * n_cu, dtype=torch.int64, device="cuda")
+    items = torch.zeros(4 * slots * n_cu, dtype=torch.int64, device="cuda")
+    ops.hdp_set_trace(trace)
+    ops.hdp_set_item_trace(items, slots)
+    try:
+        o, lse = ops.hdp_attn_chunk_partial(qg, kg, vg, 5000, 0, True, scale)   # chunk wholly in the past
+        torch.cuda.synchronize()
+    finally:
+        ops.hdp_set_trace(None)
+        ops.hdp_set_item_trace(None)
+    t = trace.view(n_cu, 4).cpu().numpy()
+    it = items.view(n_cu, slots, 4).cpu().numpy()
+    done = t[:, 2]
+    assert int(done.sum()) == math.ceil(Lq / ROWS) * (H // 4)
+    units = 0
+    for b in range(n_cu):
+        n = int(done[b])
+        for i in range(n):
+            a0, a1, a2, nu = (int(x) for x in it[b, i])
+            nxt = int(it[b, i + 1, 0]) if i + 1 < n else int(t[b, 1])
+            assert t[b, 0] <= a0 <= a1 <= a2 <= nxt
+            units += nu
+    # every key of the chunk is visible to every row: each item visits all ceil(Lk / 32) units
+    assert units == int(done.sum()) * math.ceil(Lk / UNIT)
+    rows = np.arange(0, Lq, 7)
+    ro, rl = oracle.chunk_partial(q, k, v, 5000, 0, True, scale, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    assert max_abs(o[idx], ro) <= TOL_BF16_OUT
+    lse_close(lse[idx], rl, TOL_BF16_LSE)
